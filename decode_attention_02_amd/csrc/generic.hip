@@ -1,0 +1,290 @@
+// Generic (any-shape) kernels of the GQLA decode path, fp32 or bf16 data, fp32 math.
+//
+// These cover every dims combination that fits the LDS budget, in particular the fp32
+// layer shapes; the MFMA kernels in the other files take the DeepSeek-V3 / LLaMA-3
+// production shapes. Work per thread is plain VALU arithmetic read straight from
+// global memory: simple, exact in fp32, not tuned.
+#include "device_common.h"
+#include "gqla_internal.h"
+
+#include <cmath>
+
+namespace gqla {
+
+constexpr int kGenRows = 16;      // query rows per workgroup
+constexpr int kGenThreads = 256;
+
+size_t generic_attn_lds_bytes(int dk, int dvo) {
+  return sizeof(float) * (static_cast<size_t>(kGenRows) * (dk + kBlock + dvo) + 3 * kGenRows);
+}
+
+// One workgroup = (split, row tile, sequence x kv head). Online softmax over the
+// 64-token blocks of its split: scores to LDS, row statistics, rescaled accumulation.
+template <typename T>
+__global__ __launch_bounds__(kGenThreads) void generic_attn_split(AttnParams p) {
+  extern __shared__ float smem[];
+  const int tid = threadIdx.x;
+  const int split = blockIdx.x;
+  const int r0 = blockIdx.y * kGenRows;
+  const int b = blockIdx.z / p.kv_heads;
+  const int kvh = blockIdx.z % p.kv_heads;
+  const int rows_total = p.heads_per_kv * p.s_q;
+  const int nr = min(kGenRows, rows_total - r0);
+  const T* q = static_cast<const T*>(p.q);
+  const T* kv = static_cast<const T*>(p.kv);
+
+  float* sq = smem;                        // [kGenRows][dk]
+  float* ss = sq + kGenRows * p.dk;        // [kGenRows][64]
+  float* so = ss + kGenRows * kBlock;      // [kGenRows][dvo]
+  float* sm = so + kGenRows * p.dvo;       // running max
+  float* sl = sm + kGenRows;               // running sum
+  float* sa = sl + kGenRows;               // rescale factor of the current block
+
+  const int L = p.ctx_lens[b];
+  // Metadata the launch cannot honour makes the rows NaN instead of reading past
+  // the table or silently dropping tokens.
+  bool bad = (L < p.s_q) || (L > p.max_blocks * kBlock) ||
+             ((L + kBlock - 1) / kBlock > p.n_split * p.blocks_per_split);
+
+  for (int idx = tid; idx < nr * p.dk; idx += kGenThreads) {
+    const int r = idx / p.dk, f = idx % p.dk, rr = r0 + r;
+    const int i = rr / p.heads_per_kv, h = kvh * p.heads_per_kv + rr % p.heads_per_kv;
+    sq[idx] = Elt<T>::load(q, (static_cast<int64_t>(b * p.s_q + i) * p.H + h) * p.dk + f);
+  }
+  for (int idx = tid; idx < nr * p.dvo; idx += kGenThreads) so[idx] = 0.f;
+  if (tid < kGenRows) { sm[tid] = -INFINITY; sl[tid] = 0.f; }
+  __syncthreads();
+
+  const int nblk = bad ? 0 : (L + kBlock - 1) / kBlock;
+  const int blk_lo = split * p.blocks_per_split;
+  const int blk_hi = min(nblk, blk_lo + p.blocks_per_split);
+  for (int blk = blk_lo; blk < blk_hi; ++blk) {
+    const int32_t id = p.block_table[static_cast<int64_t>(b) * p.max_blocks + blk];
+    if (id < 0 || id >= p.num_blocks) { bad = true; break; }   // uniform across the group
+    const T* base = kv + static_cast<int64_t>(id) * p.block_stride + kvh * p.kvh_stride;
+    for (int idx = tid; idx < nr * kBlock; idx += kGenThreads) {
+      const int r = idx / kBlock, t = idx % kBlock, rr = r0 + r;
+      const int n = L - p.s_q + 1 + rr / p.heads_per_kv;
+      float s = -INFINITY;
+      if (blk * kBlock + t < n) {
+        float acc = 0.f;
+        for (int f = 0; f < p.dk; ++f)
+          acc += sq[r * p.dk + f] * Elt<T>::load(base, static_cast<int64_t>(t) * p.k_ts + static_cast<int64_t>(f) * p.k_fs);
+        s = acc * p.scale;
+      }
+      ss[idx] = s;
+    }
+    __syncthreads();
+    if (tid < nr) {
+      float mx = -INFINITY;
+      for (int t = 0; t < kBlock; ++t) mx = fmaxf(mx, ss[tid * kBlock + t]);
+      const float m_old = sm[tid];
+      const float m_new = fmaxf(m_old, mx);
+      float alpha = 1.f, sum = 0.f;
+      if (m_new != -INFINITY) {
+        alpha = (m_old == -INFINITY) ? 0.f : expf(m_old - m_new);
+        for (int t = 0; t < kBlock; ++t) {
+          const float e = expf(ss[tid * kBlock + t] - m_new);
+          ss[tid * kBlock + t] = e;
+          sum += e;
+        }
+      }
+      sl[tid] = sl[tid] * alpha + sum;
+      sm[tid] = m_new;
+      sa[tid] = alpha;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < nr * p.dvo; idx += kGenThreads) {
+      const int r = idx / p.dvo, f = idx % p.dvo, rr = r0 + r;
+      const int n = L - p.s_q + 1 + rr / p.heads_per_kv;
+      const int lim = min(kBlock, n - blk * kBlock);   // tokens this row sees in the block
+      float acc = so[idx] * sa[r];
+      for (int t = 0; t < lim; ++t)
+        acc += ss[r * kBlock + t] *
+               Elt<T>::load(base, p.v_off + static_cast<int64_t>(t) * p.v_ts + static_cast<int64_t>(f) * p.v_fs);
+      so[idx] = acc;
+    }
+    __syncthreads();
+  }
+
+  for (int idx = tid; idx < nr * p.dvo; idx += kGenThreads) {
+    const int r = idx / p.dvo, f = idx % p.dvo, rr = r0 + r;
+    const int i = rr / p.heads_per_kv, h = kvh * p.heads_per_kv + rr % p.heads_per_kv;
+    const int64_t row = static_cast<int64_t>(b * p.s_q + i) * p.H + h;
+    const float l = sl[r], m = sm[r];
+    if (p.n_split == 1) {
+      store_out(p.out, p.out_kind, row * p.dvo + f, bad ? nan_f32() : so[idx] / l);
+      if (p.lse != nullptr && f == 0) p.lse[row] = bad ? nan_f32() : m + logf(l);
+    } else {
+      const int64_t slot = row * p.n_split + split;
+      p.ws_o[slot * p.dvo + f] = bad ? nan_f32() : (l > 0.f ? so[idx] / l : 0.f);
+      if (f == 0) p.ws_lse[slot] = bad ? nan_f32() : (l > 0.f ? m + logf(l) : -INFINITY);
+    }
+  }
+}
+
+hipError_t launch_generic_attn(const AttnParams& p, bool bf16, hipStream_t s) {
+  const int rows_total = p.heads_per_kv * p.s_q;
+  dim3 grid(p.n_split, (rows_total + kGenRows - 1) / kGenRows, p.B * p.kv_heads);
+  const size_t lds = generic_attn_lds_bytes(p.dk, p.dvo);
+  if (bf16) {
+    hipFuncSetAttribute(reinterpret_cast<const void*>(&generic_attn_split<bf16_t>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    generic_attn_split<bf16_t><<<grid, kGenThreads, lds, s>>>(p);
+  } else {
+    hipFuncSetAttribute(reinterpret_cast<const void*>(&generic_attn_split<float>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    generic_attn_split<float><<<grid, kGenThreads, lds, s>>>(p);
+  }
+  return hipGetLastError();
+}
+
+// Merge split partials: o = sum_s w_s o_s / sum_s w_s, w_s = exp(lse_s - max lse);
+// lse = max + ln sum w. A NaN partial (bad metadata) makes the row NaN.
+__global__ __launch_bounds__(256) void combine_splits(CombineParams c) {
+  __shared__ float w[1024];
+  __shared__ float tot_s, m_s;
+  __shared__ int nan_s;
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    float m = -INFINITY;
+    int has_nan = 0;
+    for (int s = 0; s < c.n_split; ++s) {
+      const float l = c.ws_lse[row * c.n_split + s];
+      if (l != l) has_nan = 1;
+      else m = fmaxf(m, l);
+    }
+    float tot = 0.f;
+    for (int s = 0; s < c.n_split; ++s) {
+      const float l = c.ws_lse[row * c.n_split + s];
+      const float e = (has_nan || l == -INFINITY) ? 0.f : expf(l - m);
+      w[s] = e;
+      tot += e;
+    }
+    tot_s = tot;
+    m_s = m;
+    nan_s = has_nan || !(tot > 0.f);
+  }
+  __syncthreads();
+  const float inv = 1.f / tot_s;
+  for (int f = tid; f < c.dvo; f += blockDim.x) {
+    float acc = 0.f;
+    for (int s = 0; s < c.n_split; ++s) {
+      if (w[s] != 0.f) acc += w[s] * c.ws_o[(row * c.n_split + s) * c.dvo + f];
+    }
+    store_out(c.out, c.out_kind, row * c.dvo + f, nan_s ? nan_f32() : acc * inv);
+  }
+  if (c.lse != nullptr && tid == 0) c.lse[row] = nan_s ? nan_f32() : m_s + logf(tot_s);
+}
+
+hipError_t launch_combine(const CombineParams& c, hipStream_t s) {
+  if (c.n_split > 1024) return hipErrorInvalidValue;
+  combine_splits<<<c.rows, 256, 0, s>>>(c);
+  return hipGetLastError();
+}
+
+// q_abs[row][h] = [W_UK^g^T q_nope[row][h] ; q_rope[row][h]] (one workgroup per (row, h)).
+template <typename T>
+__global__ __launch_bounds__(256) void generic_absorb_query(ProjParams d, const T* q_nope, const T* q_rope,
+                                                            const T* w_uk, T* q_abs) {
+  const int64_t rh = blockIdx.x;             // (b * s_q + i) * H + h
+  const int h = static_cast<int>(rh % d.H);
+  const int g = h / (d.H / d.G);
+  const int dq = d.dc + d.dr;
+  for (int c = threadIdx.x; c < dq; c += blockDim.x) {
+    float acc;
+    if (c < d.dc) {
+      acc = 0.f;
+      for (int n = 0; n < d.dn; ++n)
+        acc += Elt<T>::load(q_nope, rh * d.dn + n) * Elt<T>::load(w_uk, (static_cast<int64_t>(g) * d.dn + n) * d.dc + c);
+    } else {
+      acc = Elt<T>::load(q_rope, rh * d.dr + (c - d.dc));
+    }
+    Elt<T>::store(q_abs, rh * dq + c, acc);
+  }
+}
+
+hipError_t launch_generic_absorb_query(const ProjParams& d, const void* q_nope, const void* q_rope,
+                                       const void* w_uk, void* q_abs, bool bf16, hipStream_t s) {
+  const int64_t n = static_cast<int64_t>(d.rows) * d.H;
+  if (bf16)
+    generic_absorb_query<bf16_t><<<n, 256, 0, s>>>(d, static_cast<const bf16_t*>(q_nope), static_cast<const bf16_t*>(q_rope),
+                                                 static_cast<const bf16_t*>(w_uk), static_cast<bf16_t*>(q_abs));
+  else
+    generic_absorb_query<float><<<n, 256, 0, s>>>(d, static_cast<const float*>(q_nope), static_cast<const float*>(q_rope),
+                                                static_cast<const float*>(w_uk), static_cast<float*>(q_abs));
+  return hipGetLastError();
+}
+
+// out[row][h][v] = sum_c W_UV^g[v][c] o_lat[row][h][c]; one wave per output value.
+template <typename T>
+__global__ __launch_bounds__(256) void generic_out_proj(ProjParams d, const float* o_lat, const T* w_uv, T* out) {
+  const int64_t rh = blockIdx.x;
+  const int h = static_cast<int>(rh % d.H);
+  const int g = h / (d.H / d.G);
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  for (int v = wave; v < d.dv; v += blockDim.x / 64) {
+    float acc = 0.f;
+    for (int c = lane; c < d.dc; c += 64)
+      acc += o_lat[rh * d.dc + c] * Elt<T>::load(w_uv, (static_cast<int64_t>(g) * d.dv + v) * d.dc + c);
+    acc = wave_sum(acc);
+    if (lane == 0) Elt<T>::store(out, rh * d.dv + v, acc);
+  }
+}
+
+hipError_t launch_generic_out_proj(const ProjParams& d, const float* o_lat, const void* w_uv,
+                                   void* out, bool bf16, hipStream_t s) {
+  const int64_t n = static_cast<int64_t>(d.rows) * d.H;
+  if (bf16)
+    generic_out_proj<bf16_t><<<n, 256, 0, s>>>(d, o_lat, static_cast<const bf16_t*>(w_uv), static_cast<bf16_t*>(out));
+  else
+    generic_out_proj<float><<<n, 256, 0, s>>>(d, o_lat, static_cast<const float*>(w_uv), static_cast<float*>(out));
+  return hipGetLastError();
+}
+
+// Expanded chunk of (block id, group g): K [64][d_qk] token-major, then V [d_v][64].
+template <typename T>
+__global__ __launch_bounds__(256) void generic_expand(ProjParams d, const T* latent, const T* w_uk, const T* w_uv,
+                                                      const int32_t* block_ids, int64_t num_blocks, T* expanded) {
+  const int32_t id = block_ids[blockIdx.x];
+  if (id < 0 || id >= num_blocks) return;
+  const int g = blockIdx.y;
+  const int dq = d.dc + d.dr, dqk = d.dn + d.dr;
+  const T* src = latent + static_cast<int64_t>(id) * kBlock * dq;
+  T* dst = expanded + (static_cast<int64_t>(id) * d.G + g) * kBlock * (dqk + d.dv);
+  for (int idx = threadIdx.x; idx < kBlock * dqk; idx += blockDim.x) {
+    const int r = idx / dqk, e = idx % dqk;
+    float acc;
+    if (e < d.dn) {
+      acc = 0.f;
+      for (int c = 0; c < d.dc; ++c)
+        acc += Elt<T>::load(src, static_cast<int64_t>(r) * dq + c) * Elt<T>::load(w_uk, (static_cast<int64_t>(g) * d.dn + e) * d.dc + c);
+    } else {
+      acc = Elt<T>::load(src, static_cast<int64_t>(r) * dq + d.dc + (e - d.dn));
+    }
+    Elt<T>::store(dst, idx, acc);
+  }
+  for (int idx = threadIdx.x; idx < d.dv * kBlock; idx += blockDim.x) {
+    const int f = idx / kBlock, r = idx % kBlock;
+    float acc = 0.f;
+    for (int c = 0; c < d.dc; ++c)
+      acc += Elt<T>::load(src, static_cast<int64_t>(r) * dq + c) * Elt<T>::load(w_uv, (static_cast<int64_t>(g) * d.dv + f) * d.dc + c);
+    Elt<T>::store(dst, static_cast<int64_t>(kBlock) * dqk + idx, acc);
+  }
+}
+
+hipError_t launch_generic_expand(const ProjParams& d, const void* latent, const void* w_uk,
+                                 const void* w_uv, const int32_t* block_ids, int64_t n_blocks,
+                                 int64_t num_blocks, void* expanded, bool bf16, hipStream_t s) {
+  dim3 grid(static_cast<unsigned>(n_blocks), d.G);
+  if (bf16)
+    generic_expand<bf16_t><<<grid, 256, 0, s>>>(d, static_cast<const bf16_t*>(latent), static_cast<const bf16_t*>(w_uk),
+                                               static_cast<const bf16_t*>(w_uv), block_ids, num_blocks, static_cast<bf16_t*>(expanded));
+  else
+    generic_expand<float><<<grid, 256, 0, s>>>(d, static_cast<const float*>(latent), static_cast<const float*>(w_uk),
+                                              static_cast<const float*>(w_uv), block_ids, num_blocks, static_cast<float*>(expanded));
+  return hipGetLastError();
+}
+
+}  // namespace gqla

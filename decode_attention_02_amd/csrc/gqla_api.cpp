@@ -1,0 +1,350 @@
+// Host side of libgqla: argument validation, split-KV planning and kernel dispatch.
+// Nothing here allocates device memory or synchronises (except gqla_validate_paged,
+// a debug call documented as synchronous).
+#include "../../include/gqla.h"
+#include "gqla_internal.h"
+#include "tuned.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+namespace {
+
+thread_local std::string g_err;
+
+gqla_status fail(gqla_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+gqla_status hip_fail(hipError_t e, const char* where) {
+  return fail(GQLA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+gqla_status check_dims(const gqla_dims* d) {
+  if (d == nullptr) return fail(GQLA_ERR_INVALID_ARG, "dims is NULL");
+  if (d->batch < 1 || d->num_heads < 1 || d->num_groups < 1 || d->latent_rank < 1 ||
+      d->rope_dim < 0 || d->nope_dim < 1 || d->v_dim < 1)
+    return fail(GQLA_ERR_INVALID_ARG, "dimensions must be positive (rope_dim >= 0)");
+  if (d->num_heads % d->num_groups != 0)
+    return fail(GQLA_ERR_INVALID_ARG, "num_groups (%d) must divide num_heads (%d)", d->num_groups, d->num_heads);
+  if (d->s_q < 1) return fail(GQLA_ERR_INVALID_ARG, "s_q must be >= 1 (got %d)", d->s_q);
+  if (d->block_size != gqla::kBlock)
+    return fail(GQLA_ERR_INVALID_ARG, "block_size must be 64 (got %d)", d->block_size);
+  if (d->dtype != GQLA_F32 && d->dtype != GQLA_BF16)
+    return fail(GQLA_ERR_INVALID_ARG, "unknown dtype %d", d->dtype);
+  return GQLA_OK;
+}
+
+gqla_status check_path(int32_t path) {
+  if (path != GQLA_PATH_ABSORB && path != GQLA_PATH_GQA)
+    return fail(GQLA_ERR_INVALID_ARG, "unknown path %d (0 = absorb, 1 = gqa)", path);
+  return GQLA_OK;
+}
+
+gqla_status check_paged(const gqla_dims* d, const gqla_paged* p) {
+  if (p == nullptr) return fail(GQLA_ERR_INVALID_ARG, "paged is NULL");
+  if (p->block_table == nullptr || p->ctx_lens == nullptr)
+    return fail(GQLA_ERR_INVALID_ARG, "block_table and ctx_lens must be device pointers");
+  if (p->max_blocks_per_seq < 1 || p->num_blocks < 1)
+    return fail(GQLA_ERR_INVALID_ARG, "max_blocks_per_seq and num_blocks must be >= 1");
+  if (p->max_ctx_len < d->s_q)
+    return fail(GQLA_ERR_INVALID_ARG, "max_ctx_len (%d) must be >= s_q (%d)", p->max_ctx_len, d->s_q);
+  if (static_cast<int64_t>(p->max_ctx_len) > static_cast<int64_t>(p->max_blocks_per_seq) * gqla::kBlock)
+    return fail(GQLA_ERR_INVALID_ARG, "max_ctx_len (%d) exceeds max_blocks_per_seq * 64", p->max_ctx_len);
+  if (p->num_splits < 0) return fail(GQLA_ERR_INVALID_ARG, "num_splits must be >= 0");
+  return GQLA_OK;
+}
+
+float resolve_scale(const gqla_dims* d) {
+  return d->softmax_scale > 0.f ? d->softmax_scale
+                                : 1.0f / std::sqrt(static_cast<float>(d->nope_dim + d->rope_dim));
+}
+
+int elt_bytes(const gqla_dims* d) { return d->dtype == GQLA_BF16 ? 2 : 4; }
+
+struct Plan {
+  int n_split;
+  int blocks_per_split;
+  bool tuned;
+};
+
+// Split-KV plan. Units of independent work are (sequence, group) on the GQA path and
+// sequences on the absorb path; the context is cut into equal 64-token-aligned splits
+// until the launch holds enough workgroups to cover the 256 CUs, while keeping each
+// split long enough to amortise its prologue and the partial-result traffic.
+Plan plan(const gqla_dims* d, const gqla_paged* p, int32_t path) {
+  Plan pl{};
+  const int nblk = (p->max_ctx_len + gqla::kBlock - 1) / gqla::kBlock;
+  int n;
+  if (path == GQLA_PATH_GQA) {
+    pl.tuned = gqla::tuned_gqa_supported(d);
+    const int64_t units = static_cast<int64_t>(d->batch) * d->num_groups;
+    const int64_t target = pl.tuned ? gqla::tuned_gqa_target_wgs() : 2 * gqla::kNumCUs;
+    const int min_blocks = pl.tuned ? gqla::tuned_gqa_min_blocks_per_split() : 2;
+    n = static_cast<int>(std::min<int64_t>((target + units - 1) / units, std::max(1, nblk / min_blocks)));
+  } else {
+    pl.tuned = gqla::tuned_absorb_supported(d);
+    const int64_t units = pl.tuned ? d->batch
+                                   : static_cast<int64_t>(d->batch) * ((d->num_heads * d->s_q + 15) / 16);
+    const int64_t target = pl.tuned ? gqla::tuned_absorb_target_wgs(d) : 2 * gqla::kNumCUs;
+    const int min_blocks = pl.tuned ? gqla::tuned_absorb_min_blocks_per_split() : 2;
+    n = static_cast<int>(std::min<int64_t>((target + units - 1) / units, std::max(1, nblk / min_blocks)));
+  }
+  if (p->num_splits > 0) n = p->num_splits;
+  n = std::max(1, std::min(n, std::min(nblk, 1024)));
+  pl.blocks_per_split = (nblk + n - 1) / n;
+  pl.n_split = (nblk + pl.blocks_per_split - 1) / pl.blocks_per_split;
+  return pl;
+}
+
+size_t workspace_for(const gqla_dims* d, int32_t path, int n_split) {
+  if (n_split <= 1) return 0;
+  const size_t rows = static_cast<size_t>(d->batch) * d->s_q * d->num_heads;
+  const size_t dvo = path == GQLA_PATH_GQA ? d->v_dim : d->latent_rank;
+  return rows * n_split * (dvo + 1) * sizeof(float);
+}
+
+gqla_status run_decode(const gqla_dims* d, const gqla_paged* pg, int32_t path, const void* q,
+                       const void* cache, void* ws, size_t ws_bytes, void* out, int32_t out_kind,
+                       float* lse, void* stream) {
+  const Plan pl = plan(d, pg, path);
+  const size_t need = workspace_for(d, path, pl.n_split);
+  if (ws_bytes < need || (need > 0 && ws == nullptr))
+    return fail(GQLA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, need);
+  const bool gqa = path == GQLA_PATH_GQA;
+  gqla::AttnParams a{};
+  a.q = q;
+  a.kv = cache;
+  a.block_table = pg->block_table;
+  a.ctx_lens = pg->ctx_lens;
+  a.num_blocks = pg->num_blocks;
+  a.max_blocks = pg->max_blocks_per_seq;
+  a.B = d->batch;
+  a.H = d->num_heads;
+  a.s_q = d->s_q;
+  a.scale = resolve_scale(d);
+  a.n_split = pl.n_split;
+  a.blocks_per_split = pl.blocks_per_split;
+  const int rows = d->batch * d->s_q * d->num_heads;
+  if (gqa) {
+    const int dqk = d->nope_dim + d->rope_dim;
+    a.kv_heads = d->num_groups;
+    a.heads_per_kv = d->num_heads / d->num_groups;
+    a.dk = dqk;
+    a.dvo = d->v_dim;
+    a.kvh_stride = static_cast<int64_t>(gqla::kBlock) * (dqk + d->v_dim);
+    a.block_stride = a.kvh_stride * d->num_groups;
+    a.k_ts = dqk;
+    a.k_fs = 1;
+    a.v_off = gqla::kBlock * dqk;
+    a.v_ts = 1;
+    a.v_fs = gqla::kBlock;
+  } else {
+    const int dq = d->latent_rank + d->rope_dim;
+    a.kv_heads = 1;
+    a.heads_per_kv = d->num_heads;
+    a.dk = dq;
+    a.dvo = d->latent_rank;
+    a.kvh_stride = 0;
+    a.block_stride = static_cast<int64_t>(gqla::kBlock) * dq;
+    a.k_ts = dq;
+    a.k_fs = 1;
+    a.v_off = 0;
+    a.v_ts = dq;
+    a.v_fs = 1;
+  }
+  if (pl.n_split > 1) {
+    a.ws_o = static_cast<float*>(ws);
+    a.ws_lse = a.ws_o + static_cast<size_t>(rows) * pl.n_split * a.dvo;
+  }
+  a.out = out;
+  a.out_kind = out_kind;
+  a.lse = lse;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf16 = d->dtype == GQLA_BF16;
+  hipError_t e;
+  if (pl.tuned) {
+    e = gqa ? gqla::launch_tuned_gqa(a, d, s) : gqla::launch_tuned_absorb(a, d, s);
+  } else {
+    if (gqla::generic_attn_lds_bytes(a.dk, a.dvo) > 160 * 1024)
+      return fail(GQLA_ERR_UNSUPPORTED, "key width %d + value width %d exceed the generic kernel's LDS budget", a.dk, a.dvo);
+    e = gqla::launch_generic_attn(a, bf16, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, gqa ? "gqa split-KV decode launch" : "absorb split-KV decode launch");
+  if (pl.n_split > 1) {
+    gqla::CombineParams c{a.ws_o, a.ws_lse, rows, pl.n_split, a.dvo, out, out_kind, lse};
+    e = gqla::launch_combine(c, s);
+    if (e != hipSuccess) return hip_fail(e, "split-KV combine launch");
+  }
+  return GQLA_OK;
+}
+
+gqla::ProjParams proj_params(const gqla_dims* d) {
+  gqla::ProjParams p{};
+  p.rows = d->batch * d->s_q;
+  p.H = d->num_heads;
+  p.G = d->num_groups;
+  p.dc = d->latent_rank;
+  p.dr = d->rope_dim;
+  p.dn = d->nope_dim;
+  p.dv = d->v_dim;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+gqla_status gqla_absorb_query(const gqla_dims* dims, const void* q_nope, const void* q_rope,
+                              const void* w_uk, void* q_abs, void* stream) {
+  gqla_status st = check_dims(dims);
+  if (st != GQLA_OK) return st;
+  if (!q_nope || !w_uk || !q_abs || (dims->rope_dim > 0 && !q_rope))
+    return fail(GQLA_ERR_INVALID_ARG, "null tensor pointer");
+  const gqla::ProjParams p = proj_params(dims);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = gqla::tuned_absorb_query_supported(dims)
+                     ? gqla::launch_tuned_absorb_query(p, q_nope, q_rope, w_uk, q_abs, s)
+                     : gqla::launch_generic_absorb_query(p, q_nope, q_rope, w_uk, q_abs, dims->dtype == GQLA_BF16, s);
+  return e == hipSuccess ? GQLA_OK : hip_fail(e, "absorb query launch");
+}
+
+gqla_status gqla_decode_absorb(const gqla_dims* dims, const gqla_paged* paged, const void* q_abs,
+                               const void* latent_cache, void* workspace, size_t workspace_bytes,
+                               float* o_lat, float* lse, void* stream) {
+  gqla_status st = check_dims(dims);
+  if (st != GQLA_OK) return st;
+  if ((st = check_paged(dims, paged)) != GQLA_OK) return st;
+  if (!q_abs || !latent_cache || !o_lat) return fail(GQLA_ERR_INVALID_ARG, "null tensor pointer");
+  return run_decode(dims, paged, GQLA_PATH_ABSORB, q_abs, latent_cache, workspace, workspace_bytes,
+                    o_lat, gqla::OUT_F32, lse, stream);
+}
+
+gqla_status gqla_out_proj(const gqla_dims* dims, const float* o_lat, const void* w_uv, void* out,
+                          void* stream) {
+  gqla_status st = check_dims(dims);
+  if (st != GQLA_OK) return st;
+  if (!o_lat || !w_uv || !out) return fail(GQLA_ERR_INVALID_ARG, "null tensor pointer");
+  const gqla::ProjParams p = proj_params(dims);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = gqla::tuned_out_proj_supported(dims)
+                     ? gqla::launch_tuned_out_proj(p, o_lat, w_uv, out, s)
+                     : gqla::launch_generic_out_proj(p, o_lat, w_uv, out, dims->dtype == GQLA_BF16, s);
+  return e == hipSuccess ? GQLA_OK : hip_fail(e, "out projection launch");
+}
+
+gqla_status gqla_expand_cache(const gqla_dims* dims, const void* latent_cache, const void* w_uk,
+                              const void* w_uv, const int32_t* block_ids, int64_t n_blocks,
+                              int64_t num_blocks, void* expanded_cache, void* stream) {
+  gqla_status st = check_dims(dims);
+  if (st != GQLA_OK) return st;
+  if (n_blocks < 0 || num_blocks < 1) return fail(GQLA_ERR_INVALID_ARG, "n_blocks must be >= 0 and num_blocks >= 1");
+  if (n_blocks > 0x7fffffff) return fail(GQLA_ERR_INVALID_ARG, "at most 2^31 - 1 blocks per call");
+  if (n_blocks == 0) return GQLA_OK;
+  if (!latent_cache || !w_uk || !w_uv || !block_ids || !expanded_cache)
+    return fail(GQLA_ERR_INVALID_ARG, "null tensor pointer");
+  const gqla::ProjParams p = proj_params(dims);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = gqla::tuned_expand_supported(dims)
+                     ? gqla::launch_tuned_expand(p, latent_cache, w_uk, w_uv, block_ids, n_blocks, num_blocks, expanded_cache, s)
+                     : gqla::launch_generic_expand(p, latent_cache, w_uk, w_uv, block_ids, n_blocks, num_blocks,
+                                                   expanded_cache, dims->dtype == GQLA_BF16, s);
+  return e == hipSuccess ? GQLA_OK : hip_fail(e, "cache expansion launch");
+}
+
+gqla_status gqla_decode_gqa(const gqla_dims* dims, const gqla_paged* paged, const void* q,
+                            const void* expanded_cache, void* workspace, size_t workspace_bytes,
+                            void* out, float* lse, void* stream) {
+  gqla_status st = check_dims(dims);
+  if (st != GQLA_OK) return st;
+  if ((st = check_paged(dims, paged)) != GQLA_OK) return st;
+  if (!q || !expanded_cache || !out) return fail(GQLA_ERR_INVALID_ARG, "null tensor pointer");
+  return run_decode(dims, paged, GQLA_PATH_GQA, q, expanded_cache, workspace, workspace_bytes, out,
+                    dims->dtype == GQLA_BF16 ? gqla::OUT_BF16 : gqla::OUT_F32, lse, stream);
+}
+
+gqla_status gqla_num_splits(const gqla_dims* dims, const gqla_paged* paged, int32_t path, int32_t* n) {
+  gqla_status st = check_dims(dims);
+  if (st != GQLA_OK) return st;
+  if ((st = check_path(path)) != GQLA_OK) return st;
+  if (n == nullptr) return fail(GQLA_ERR_INVALID_ARG, "n is NULL");
+  if (paged == nullptr) return fail(GQLA_ERR_INVALID_ARG, "paged is NULL");
+  gqla_paged tmp = *paged;  // only the host-known fields matter here
+  tmp.block_table = reinterpret_cast<const int32_t*>(1);
+  tmp.ctx_lens = reinterpret_cast<const int32_t*>(1);
+  if ((st = check_paged(dims, &tmp)) != GQLA_OK) return st;
+  *n = plan(dims, &tmp, path).n_split;
+  return GQLA_OK;
+}
+
+gqla_status gqla_workspace_bytes(const gqla_dims* dims, const gqla_paged* paged, int32_t path,
+                                 size_t* bytes) {
+  int32_t n = 0;
+  if (bytes == nullptr) return fail(GQLA_ERR_INVALID_ARG, "bytes is NULL");
+  gqla_status st = gqla_num_splits(dims, paged, path, &n);
+  if (st != GQLA_OK) return st;
+  *bytes = workspace_for(dims, path, n);
+  return GQLA_OK;
+}
+
+int64_t gqla_cache_bytes_per_token(const gqla_dims* dims, int32_t path) {
+  if (check_dims(dims) != GQLA_OK || check_path(path) != GQLA_OK) return 0;
+  const int64_t elt = elt_bytes(dims);
+  if (path == GQLA_PATH_ABSORB) return (dims->latent_rank + dims->rope_dim) * elt;
+  return static_cast<int64_t>(dims->num_groups) * (dims->nope_dim + dims->rope_dim + dims->v_dim) * elt;
+}
+
+gqla_status gqla_validate_paged(const gqla_dims* dims, const gqla_paged* paged, void* stream) {
+  gqla_status st = check_dims(dims);
+  if (st != GQLA_OK) return st;
+  if ((st = check_paged(dims, paged)) != GQLA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  std::vector<int32_t> lens(dims->batch);
+  std::vector<int32_t> table(static_cast<size_t>(dims->batch) * paged->max_blocks_per_seq);
+  hipError_t e = hipMemcpyAsync(lens.data(), paged->ctx_lens, lens.size() * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(table.data(), paged->block_table, table.size() * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "reading paged metadata");
+  for (int b = 0; b < dims->batch; ++b) {
+    const int L = lens[b];
+    if (L < dims->s_q || L > paged->max_ctx_len)
+      return fail(GQLA_ERR_INVALID_ARG, "ctx_lens[%d] = %d outside [s_q = %d, max_ctx_len = %d]", b, L,
+                  dims->s_q, paged->max_ctx_len);
+    for (int k = 0; k < (L + gqla::kBlock - 1) / gqla::kBlock; ++k) {
+      const int32_t id = table[static_cast<size_t>(b) * paged->max_blocks_per_seq + k];
+      if (id < 0 || id >= paged->num_blocks)
+        return fail(GQLA_ERR_INVALID_ARG, "block_table[%d][%d] = %d outside [0, %lld)", b, k, id,
+                    static_cast<long long>(paged->num_blocks));
+    }
+  }
+  return GQLA_OK;
+}
+
+const char* gqla_status_string(gqla_status status) {
+  switch (status) {
+    case GQLA_OK: return "ok";
+    case GQLA_ERR_INVALID_ARG: return "invalid argument";
+    case GQLA_ERR_UNSUPPORTED: return "unsupported dimensions";
+    case GQLA_ERR_WORKSPACE: return "workspace too small";
+    case GQLA_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* gqla_last_error(void) { return g_err.c_str(); }
+
+const char* gqla_version(void) { return "gqla-mi355x 0.1 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,66 @@
+// Internal declarations shared by the host API and the HIP kernels of libgqla.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace gqla {
+
+constexpr int kBlock = 64;        // tokens per cache block
+constexpr int kNumCUs = 256;      // MI355X compute units (split-KV planning)
+
+enum OutKind : int32_t { OUT_F32 = 0, OUT_BF16 = 1 };
+
+// One split-KV attention launch. A "kv head" is the latent (absorb path, 1 per
+// sequence) or one group's expanded K/V (GQA path, G per sequence). Row r of a kv head
+// is query row i = r / heads_per_kv of head h = kvh * heads_per_kv + r % heads_per_kv.
+struct AttnParams {
+  const void* q;                 // [B][s_q][H][dk] data
+  const void* kv;                // cache pool base (data)
+  const int32_t* block_table;    // [B][max_blocks]
+  const int32_t* ctx_lens;       // [B]
+  int64_t num_blocks;
+  int64_t block_stride;          // elements per physical block
+  int64_t kvh_stride;            // elements between kv heads inside a block
+  int32_t max_blocks;
+  int32_t B, H, s_q;
+  int32_t kv_heads, heads_per_kv;
+  int32_t dk, dvo;               // key width, value/output width
+  int32_t k_ts, k_fs;            // K(t, f) at k_ts * t + k_fs * f
+  int32_t v_off, v_ts, v_fs;     // V(t, f) at v_off + v_ts * t + v_fs * f
+  float scale;
+  int32_t n_split, blocks_per_split;
+  float* ws_o;                   // [B*s_q*H][n_split][dvo]   (n_split > 1)
+  float* ws_lse;                 // [B*s_q*H][n_split]        (n_split > 1)
+  void* out;                     // [B*s_q*H][dvo]            (n_split == 1)
+  int32_t out_kind;              // OutKind of `out`
+  float* lse;                    // [B*s_q*H] or null         (n_split == 1)
+};
+
+struct CombineParams {
+  const float* ws_o;
+  const float* ws_lse;
+  int32_t rows, n_split, dvo;
+  void* out;
+  int32_t out_kind;
+  float* lse;
+};
+
+struct ProjParams {
+  int32_t rows;                  // B * s_q
+  int32_t H, G, dc, dr, dn, dv;
+};
+
+// Generic kernels: any dims that fit the LDS budget, fp32 or bf16 data.
+hipError_t launch_generic_attn(const AttnParams& p, bool bf16, hipStream_t s);
+size_t generic_attn_lds_bytes(int dk, int dvo);
+hipError_t launch_combine(const CombineParams& c, hipStream_t s);
+hipError_t launch_generic_absorb_query(const ProjParams& d, const void* q_nope, const void* q_rope,
+                                       const void* w_uk, void* q_abs, bool bf16, hipStream_t s);
+hipError_t launch_generic_out_proj(const ProjParams& d, const float* o_lat, const void* w_uv,
+                                   void* out, bool bf16, hipStream_t s);
+hipError_t launch_generic_expand(const ProjParams& d, const void* latent, const void* w_uk,
+                                 const void* w_uv, const int32_t* block_ids, int64_t n_blocks,
+                                 int64_t num_blocks, void* expanded, bool bf16, hipStream_t s);
+
+}  // namespace gqla

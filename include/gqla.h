@@ -1,0 +1,198 @@
+/*
+ * gqla.h — C ABI of libgqla.so: the decode-attention hot path of Group-Query Latent
+ * Attention (GQLA) on AMD Instinct MI355X (gfx950).
+ *
+ * GQLA caches MLA's joint low-rank latent c_KV per token and gives each group of
+ * gs = H / G query heads one shared key up-projection W_UK^g and one shared value
+ * up-projection W_UV^g ("GQLA: Group-Query Latent Attention for Hardware-Adaptive
+ * Decoding", Abstract). The same weights decode two algebraically equivalent ways
+ * ("GQLA: Attention latente par requêtes groupées ...", English abstract):
+ *
+ *   (a) MQA-absorb: gqla_absorb_query -> gqla_decode_absorb -> gqla_out_proj.
+ *       W_UK^g is folded into every query, all heads attend over the cached latent,
+ *       and W_UV^g is applied to each head's latent output.
+ *   (b) GQA: gqla_expand_cache (when latent blocks are filled) -> gqla_decode_gqa.
+ *       The latent is expanded into G key/value heads that the gs query heads of each
+ *       group share ("Grouped Query Attention (GQA)", section "Fonctionnement de la GQA").
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Dimensions: B batch, H query heads, G groups (G divides H; head h is in group
+ * h / gs), d_c latent rank, d_R RoPE dim, d_n nope dim, d_qk = d_n + d_R, d_v value
+ * dim, s_q query rows per sequence (1, or 2 for multi-token prediction).
+ *
+ * Element type: every tensor marked "data" is float (GQLA_F32) or bfloat16 (GQLA_BF16)
+ * as dims->dtype says; accumulation is always fp32. o_lat, lse and the workspace are
+ * always fp32. Index tensors are int32.
+ *
+ * Memory: every pointer except dims/paged and the `bytes`/`n` out-parameters is DEVICE
+ * memory owned by the caller, contiguous in the layout stated. The library allocates
+ * nothing, keeps no state between calls beyond a thread-local error string, and never
+ * synchronises: work is enqueued on `stream` (a hipStream_t; NULL = default stream).
+ * Calls may be captured in a HIP graph (no memset nodes are recorded).
+ *
+ * Paged caches: tokens live in fixed 64-token blocks ("Grouped Query Attention (GQA)",
+ * section "GQA et techniques connexes", PagedAttention). Logical token t of sequence b
+ * is slot t % 64 of physical block block_table[b][t / 64].
+ *
+ * Causality: ctx_lens[b] = L_b counts the s_q new tokens. Query row i (0 <= i < s_q)
+ * of sequence b sees tokens 0 .. L_b - s_q + i.
+ *
+ * Softmax scale: dims->softmax_scale, or 1/sqrt(d_n + d_R) when it is <= 0; the same
+ * value must be used on both paths for them to agree.
+ *
+ * Errors: calls return a gqla_status and never abort. Host-visible argument problems
+ * (null pointer, H % G != 0, s_q < 1, block_size != 64, non-positive dims, unknown
+ * dtype or path, workspace too small, dims the kernels do not cover) are reported
+ * before anything is launched. Device-side metadata is guarded inside the kernels:
+ * a block id outside [0, num_blocks) is never dereferenced, and every output row that
+ * would have read it, or that sees no token (L_b < s_q), or whose L_b exceeds
+ * max_blocks_per_seq * 64 is written as NaN. gqla_last_error() gives a message for the
+ * most recent failing call on the calling thread.
+ */
+#ifndef GQLA_H
+#define GQLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gqla_status {
+  GQLA_OK = 0,
+  GQLA_ERR_INVALID_ARG = -1,  /* bad argument; nothing launched */
+  GQLA_ERR_UNSUPPORTED = -2,  /* valid dims that no kernel covers; nothing launched */
+  GQLA_ERR_WORKSPACE = -3,    /* workspace smaller than gqla_workspace_bytes() */
+  GQLA_ERR_HIP = -4           /* a HIP launch or runtime call failed */
+} gqla_status;
+
+typedef enum gqla_dtype { GQLA_F32 = 0, GQLA_BF16 = 1 } gqla_dtype;
+
+typedef enum gqla_path { GQLA_PATH_ABSORB = 0, GQLA_PATH_GQA = 1 } gqla_path;
+
+/* Shape of one GQLA attention layer at decode time. */
+typedef struct gqla_dims {
+  int32_t batch;        /* B   >= 1 */
+  int32_t num_heads;    /* H   >= 1 */
+  int32_t num_groups;   /* G   >= 1, divides H */
+  int32_t latent_rank;  /* d_c >= 1 */
+  int32_t rope_dim;     /* d_R >= 0 */
+  int32_t nope_dim;     /* d_n >= 1 */
+  int32_t v_dim;        /* d_v >= 1 */
+  int32_t s_q;          /* >= 1 query rows per sequence */
+  int32_t block_size;   /* tokens per cache block; must be 64 */
+  int32_t dtype;        /* gqla_dtype of every "data" tensor */
+  float softmax_scale;  /* <= 0 selects 1/sqrt(d_n + d_R) */
+} gqla_dims;
+
+/* Paged-cache metadata for one decode batch. */
+typedef struct gqla_paged {
+  const int32_t* block_table; /* device int32 [B][max_blocks_per_seq]; entries past a
+                                 sequence's last block are never read */
+  const int32_t* ctx_lens;    /* device int32 [B]; L_b, includes the s_q new tokens */
+  int32_t max_blocks_per_seq; /* row length of block_table, >= 1 */
+  int32_t max_ctx_len;        /* host-known upper bound on every L_b, >= s_q; sizes the
+                                 split-KV plan and must not be exceeded */
+  int64_t num_blocks;         /* physical blocks in the cache pool, >= 1 */
+  int32_t num_splits;         /* 0: automatic split-KV plan; k > 0: k splits */
+} gqla_paged;
+
+/*
+ * gqla_absorb_query — fold W_UK^g into the queries (MQA-absorb path, step 1).
+ *   q_abs[b][i][h] = [ W_UK^g^T q_nope[b][i][h] ; q_rope[b][i][h] ],  g = h / gs.
+ * ("GQLA: Attention latente ...", English abstract: the MQA-absorb path is MLA's
+ * absorbed form; gqla_attn.py docstring: the up-projection is absorbed into the query.)
+ *   q_nope : data [B][s_q][H][d_n]
+ *   q_rope : data [B][s_q][H][d_R]   (already rotated to the row's position)
+ *   w_uk   : data [G][d_n][d_c]      (out x in, like a linear layer's weight)
+ *   q_abs  : data [B][s_q][H][d_c + d_R]   (output, rounded to the data type)
+ */
+gqla_status gqla_absorb_query(const gqla_dims* dims, const void* q_nope, const void* q_rope,
+                              const void* w_uk, void* q_abs, void* stream);
+
+/*
+ * gqla_decode_absorb — every head attends over the shared latent "key head" (step 2).
+ *   s_t = scale * <q_abs[b][i][h], [c_t | kr_t]>,  o_lat = sum_t softmax(s)_t c_t,
+ * over the visible tokens t of row i; split-KV with an online-softmax merge.
+ *   q_abs        : data [B][s_q][H][d_c + d_R]
+ *   latent_cache : data [num_blocks][64][d_c + d_R]; row = [c_KV (d_c) | k_rope (d_R)]
+ *   workspace    : fp32 scratch of at least gqla_workspace_bytes(.., GQLA_PATH_ABSORB)
+ *                  bytes (may be NULL when that is 0)
+ *   o_lat        : fp32 [B][s_q][H][d_c]  (output)
+ *   lse          : fp32 [B][s_q][H] log-sum-exp of the scaled scores (output; NULL = skip)
+ */
+gqla_status gqla_decode_absorb(const gqla_dims* dims, const gqla_paged* paged,
+                               const void* q_abs, const void* latent_cache, void* workspace,
+                               size_t workspace_bytes, float* o_lat, float* lse, void* stream);
+
+/*
+ * gqla_out_proj — apply W_UV^g to each head's latent output (step 3).
+ *   out[b][i][h] = W_UV^g o_lat[b][i][h],  g = h / gs.
+ *   o_lat : fp32 [B][s_q][H][d_c];  w_uv : data [G][d_v][d_c];  out : data [B][s_q][H][d_v]
+ */
+gqla_status gqla_out_proj(const gqla_dims* dims, const float* o_lat, const void* w_uv,
+                          void* out, void* stream);
+
+/*
+ * gqla_expand_cache — expand latent blocks into the per-group K/V cache (GQA path).
+ * For each listed block p, group g and slot r (gqla_attn.py docstring: the latent is
+ * expanded into num_groups full key/value heads):
+ *   K[p][g][r] = [ W_UK^g c_r ; kr_r ]   (d_qk values; the RoPE key is copied per group)
+ *   V[p][g][r] =   W_UV^g c_r            (d_v values)
+ *   latent_cache   : data [num_blocks][64][d_c + d_R]
+ *   w_uk, w_uv     : data [G][d_n][d_c], [G][d_v][d_c]
+ *   block_ids      : device int32 [n_blocks], physical blocks to (re)expand; ids outside
+ *                    [0, num_blocks) are skipped
+ *   expanded_cache : data [num_blocks][G][64*d_qk + d_v*64]; per (block, group) chunk:
+ *                    K token-major [64][d_qk] (k_nope | k_rope), then V feature-major
+ *                    [d_v][64] (value feature f of slot r at f*64 + r)
+ */
+gqla_status gqla_expand_cache(const gqla_dims* dims, const void* latent_cache, const void* w_uk,
+                              const void* w_uv, const int32_t* block_ids, int64_t n_blocks,
+                              int64_t num_blocks, void* expanded_cache, void* stream);
+
+/*
+ * gqla_decode_gqa — grouped-query decode over the expanded cache.
+ *   out[b][i][h] = sum_t softmax(scale * <q[b][i][h], K[g]_t>)_t V[g]_t,  g = h / gs,
+ * over the visible tokens t of row i; split-KV with an online-softmax merge.
+ *   q              : data [B][s_q][H][d_qk] = [q_nope | q_rope]
+ *   expanded_cache : layout of gqla_expand_cache
+ *   workspace      : fp32 scratch of at least gqla_workspace_bytes(.., GQLA_PATH_GQA)
+ *   out            : data [B][s_q][H][d_v]  (output)
+ *   lse            : fp32 [B][s_q][H] (output; NULL = skip)
+ */
+gqla_status gqla_decode_gqa(const gqla_dims* dims, const gqla_paged* paged, const void* q,
+                            const void* expanded_cache, void* workspace, size_t workspace_bytes,
+                            void* out, float* lse, void* stream);
+
+/* Number of KV splits the decode call for `path` will use (host arithmetic only). */
+gqla_status gqla_num_splits(const gqla_dims* dims, const gqla_paged* paged, int32_t path,
+                            int32_t* n);
+
+/* Workspace bytes the decode call for `path` needs (0 when it runs unsplit). */
+gqla_status gqla_workspace_bytes(const gqla_dims* dims, const gqla_paged* paged, int32_t path,
+                                 size_t* bytes);
+
+/* Cache bytes per token per layer: latent (d_c + d_R) * elt for the absorb path,
+ * G * (d_qk + d_v) * elt for the GQA path; 0 for invalid arguments. */
+int64_t gqla_cache_bytes_per_token(const gqla_dims* dims, int32_t path);
+
+/* Synchronous debug check of device-side paged metadata: copies block_table and ctx_lens
+ * to the host and verifies s_q <= L_b <= min(max_ctx_len, 64 * max_blocks_per_seq) and
+ * 0 <= id < num_blocks for every block a sequence uses. Returns GQLA_ERR_INVALID_ARG with
+ * the first offending (b, block) in gqla_last_error(). */
+gqla_status gqla_validate_paged(const gqla_dims* dims, const gqla_paged* paged, void* stream);
+
+const char* gqla_status_string(gqla_status status);
+const char* gqla_last_error(void);
+
+/* Library version string. */
+const char* gqla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQLA_H */
