@@ -1,0 +1,216 @@
+"""Decode-attention benchmark of the GQLA hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic, seeded input:
+  1. gqla_expand_cache of the blocks that hold each sequence's s_q new tokens,
+  2. MQA-absorb path at s_q = 1: gqla_absorb_query -> gqla_decode_absorb -> gqla_out_proj,
+  3. GQA path at s_q = 2:        gqla_decode_gqa over the expanded cache.
+`value` = decode tokens produced per second by the step (B*1 absorb + B*2 GQA tokens).
+Per-path tokens/s and KV-read GB/s are reported under "paths"; "roofline" covers the
+dominant kernel (the GQA split-KV decode), timed with HIP events on the stream it runs
+on; "cpu_baseline" times the fp64 oracle on a bounded sample of the same batch.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama3-8b-b32-ctx8k")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--absorb-sq", type=int, default=1)
+    ap.add_argument("--gqa-sq", type=int, default=2)
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(x, q_abs_sq, gqa_sq, budget_s):
+    """Time the fp64 oracle (as it stands) on whole sequences of the batch until the
+    budget is spent: absorb path at q_abs_sq rows plus GQA path at gqa_sq rows."""
+    from threadpoolctl import threadpool_info
+    from oracle import gqla_ref as R
+    from workloads import queries_for
+    w = x.w
+    sc = R.qk_scale(w.nope, w.rope)
+    wk, wv = x.f64(x.w_uk), x.f64(x.w_uv)
+    qn1, qr1 = queries_for(x, q_abs_sq)
+    qg = x.f64(x.q)
+    done, tokens, t_total = 0, 0, 0.0
+    for b in range(len(x.ctx_lens)):
+        c, kr = x.f64(x.c_kv_seq[b]), x.f64(x.k_rope_seq[b])
+        qn, qr = x.f64(qn1[b]), x.f64(qr1[b])
+        t0 = time.perf_counter()
+        qa = R.absorb_query(qn, qr, wk)
+        o_lat, _ = R.absorb_attention(qa, c, kr, q_abs_sq, sc)
+        R.out_projection(o_lat, wv)
+        K, V = R.expand_latent(c, kr, wk, wv)
+        R.gqa_attention(qg[b], K, V, gqa_sq, sc)
+        t_total += time.perf_counter() - t0
+        done += 1
+        tokens += q_abs_sq + gqa_sq
+        if t_total >= budget_s:
+            break
+    threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    return {"value": tokens / t_total, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {len(x.ctx_lens)} sequences (context {int(x.ctx_lens[0])}), absorb s_q={q_abs_sq} "
+                      f"+ GQA s_q={gqa_sq} per sequence, fp64 NumPy, {t_total:.1f} s",
+            "host_cpus": os.cpu_count()}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {a.gpus} is not supported (this build has no "
+              "multi-GPU path; the GQA path would shard its groups across ranks)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import decode_attention_02_amd as G
+    from workloads import generate, queries_for, workload
+
+    torch.cuda.set_device(0)
+    w = workload(a.workload)
+    log(f"[bench] generating {w.name} (B={w.batch}, ctx={w.ctx}) ...")
+    t0 = time.time()
+    x = generate(w, a.gqa_sq)
+    qn1, qr1 = queries_for(x, a.absorb_sq)
+    log(f"[bench] generated in {time.time() - t0:.1f} s; uploading")
+
+    def dev(arr):
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+
+    B, H = w.batch, w.heads
+    cache, w_uk, w_uv = dev(x.latent_cache), dev(x.w_uk), dev(x.w_uv)
+    q_nope1, q_rope1 = dev(qn1), dev(qr1)
+    q_g = dev(x.q)
+    table = torch.from_numpy(x.block_table).cuda()
+    lens = torch.from_numpy(x.ctx_lens).cuda()
+    max_ctx = int(x.ctx_lens.max())
+    paged = G.Paged(table, lens, max_ctx, x.num_blocks)
+    mk = dict(batch=B, num_heads=H, num_groups=w.groups, latent_rank=w.latent, rope_dim=w.rope,
+              nope_dim=w.nope, v_dim=w.v, dtype=G.GQLA_BF16)
+    d_abs = G.Dims(s_q=a.absorb_sq, **mk)
+    d_gqa = G.Dims(s_q=a.gqa_sq, **mk)
+
+    def workspace(d, path):
+        n = G.gqla_workspace_bytes(d, path, table.shape[1], max_ctx, x.num_blocks)
+        return torch.zeros(max(n // 4, 1), dtype=torch.float32, device="cuda") if n else None
+
+    ws_abs, ws_gqa = workspace(d_abs, G.GQLA_PATH_ABSORB), workspace(d_gqa, G.GQLA_PATH_GQA)
+    splits = {"absorb": G.gqla_num_splits(d_abs, 0, table.shape[1], max_ctx, x.num_blocks),
+              "gqa": G.gqla_num_splits(d_gqa, 1, table.shape[1], max_ctx, x.num_blocks)}
+    per_block = w.groups * 64 * (w.qk + w.v)
+    expanded = torch.empty(x.num_blocks * per_block, dtype=torch.bfloat16, device="cuda")
+    all_ids = torch.arange(x.num_blocks, dtype=torch.int32, device="cuda")
+    G.gqla_expand_cache(d_gqa, cache, w_uk, w_uv, all_ids, x.num_blocks, expanded)
+    # blocks holding the s_q newest tokens of every sequence (re-expanded each step)
+    tail = set()
+    for b in range(B):
+        L = int(x.ctx_lens[b])
+        for t in range(L - a.gqa_sq, L):
+            tail.add(int(x.block_table[b, t // 64]))
+    tail_ids = torch.tensor(sorted(tail), dtype=torch.int32, device="cuda")
+
+    q_abs = torch.empty(B, a.absorb_sq, H, w.latent + w.rope, dtype=torch.bfloat16, device="cuda")
+    o_lat = torch.empty(B, a.absorb_sq, H, w.latent, dtype=torch.float32, device="cuda")
+    out_abs = torch.empty(B, a.absorb_sq, H, w.v, dtype=torch.bfloat16, device="cuda")
+    out_gqa = torch.empty(B, a.gqa_sq, H, w.v, dtype=torch.bfloat16, device="cuda")
+    lse_gqa = torch.empty(B, a.gqa_sq, H, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    marks = []
+
+    def step(record):
+        ev = [E() for _ in range(4)] if record else None
+        if record: ev[0].record()
+        G.gqla_expand_cache(d_gqa, cache, w_uk, w_uv, tail_ids, x.num_blocks, expanded)
+        if record: ev[1].record()
+        G.gqla_absorb_query(d_abs, q_nope1, q_rope1, w_uk, q_abs)
+        G.gqla_decode_absorb(d_abs, paged, q_abs, cache, ws_abs, o_lat)
+        G.gqla_out_proj(d_abs, o_lat, w_uv, out_abs)
+        if record: ev[2].record()
+        G.gqla_decode_gqa(d_gqa, paged, q_g, expanded, ws_gqa, out_gqa, lse_gqa)
+        if record:
+            ev[3].record()
+            marks.append(ev)
+
+    log(f"[bench] warmup {a.warmup} steps, splits {splits}")
+    for _ in range(a.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    start, end = E(), E()
+    log(f"[bench] timing {a.steps} steps")
+    start.record()
+    for _ in range(a.steps):
+        step(True)
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / a.steps
+    t_exp = np.mean([m[0].elapsed_time(m[1]) for m in marks])
+    t_abs = np.mean([m[1].elapsed_time(m[2]) for m in marks])
+    t_gqa = np.mean([m[2].elapsed_time(m[3]) for m in marks])
+    log(f"[bench] ms/step {ms_step:.4f}: expand {t_exp:.4f} absorb {t_abs:.4f} gqa {t_gqa:.4f}")
+
+    ctx = x.ctx_lens.astype(np.int64)
+    elt = 2
+    kv_abs = float(ctx.sum() * (w.latent + w.rope) * elt)
+    kv_gqa = float(ctx.sum() * w.groups * (w.qk + w.v) * elt)
+    vis = lambda s_q: float(sum(sum(L - s_q + 1 + i for i in range(s_q)) for L in ctx))  # noqa: E731
+    fl_abs = vis(a.absorb_sq) * H * 2 * (2 * w.latent + w.rope)
+    fl_gqa = vis(a.gqa_sq) * H * 2 * (w.qk + w.v)
+    tok_step = B * (a.absorb_sq + a.gqa_sq)
+    res = {
+        "metric": "decode attention tokens/s + KV-read HBM GB/s (% of peak), per path, at batch x context",
+        "value": tok_step / (ms_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "context": int(ctx.max()), "heads": H,
+                   "groups": w.groups, "latent": w.latent, "rope": w.rope, "nope": w.nope, "v": w.v,
+                   "s_q": {"absorb": a.absorb_sq, "gqa": a.gqa_sq},
+                   "block_table": "shuffled" if w.shuffled else "identity", "block_size": 64,
+                   "splits": splits},
+        "paths": {
+            "absorb": {"s_q": a.absorb_sq, "ms": t_abs, "tokens_per_s": B * a.absorb_sq / (t_abs / 1e3),
+                       "kv_bytes": kv_abs, "kv_GBps": kv_abs / (t_abs / 1e3) / 1e9,
+                       "hbm_frac": kv_abs / (t_abs / 1e3) / 1e9 / HBM_PEAK_GBS,
+                       "flops": fl_abs, "mfma_frac": fl_abs / (t_abs / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+            "gqa": {"s_q": a.gqa_sq, "ms": t_gqa, "tokens_per_s": B * a.gqa_sq / (t_gqa / 1e3),
+                    "kv_bytes": kv_gqa, "kv_GBps": kv_gqa / (t_gqa / 1e3) / 1e9,
+                    "hbm_frac": kv_gqa / (t_gqa / 1e3) / 1e9 / HBM_PEAK_GBS,
+                    "flops": fl_gqa, "mfma_frac": fl_gqa / (t_gqa / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+            "expand_tail": {"blocks": int(tail_ids.numel()), "ms": t_exp},
+        },
+        "roofline": {"kernel": "gqa_decode_split (gqla_decode_gqa)", "bound": "hbm",
+                     "achieved": kv_gqa / (t_gqa / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": kv_gqa / (t_gqa / 1e3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": kv_gqa, "avg_launch_ms": t_gqa},
+    }
+    if not a.no_cpu_baseline:
+        log(f"[bench] timing the fp64 oracle for ~{a.cpu_seconds:.0f} s")
+        res["cpu_baseline"] = cpu_baseline(x, a.absorb_sq, a.gqa_sq, a.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,262 @@
+// GQA-path split-KV decode on gfx950 MFMA (bf16 data, fp32 accumulation).
+//
+// Grouped-query attention over the per-group expanded cache: the gs query heads of a
+// group share one key head and one value head ("Grouped Query Attention (GQA)", section
+// "Fonctionnement de la GQA"), and GQLA's GQA path runs exactly that over the latent
+// expanded into G key/value heads ("GQLA: Attention latente ...", English abstract).
+//
+// Decode is bound by reading the cache ("Pourquoi la GQA réduit le cache KV"), so the
+// kernel is built around streaming each (block, group) chunk of 64 tokens x
+// (d_qk + d_v) bf16 exactly once, with 128-bit loads straight into MFMA operand
+// registers:
+//   * one workgroup = (sequence, group, split); its 4 waves take interleaved 64-token
+//     blocks of the split and keep private online-softmax states, merged in LDS at
+//     the end;
+//   * scores are formed transposed, S^T = K Q^T (v_mfma_f32_16x16x32_bf16, A = 16
+//     tokens x 32 features of K, B = 32 features x 16 query rows), so each lane owns
+//     one query row: its running max/sum need only two cross-lane shuffles per step;
+//   * K rows are gathered in a permuted token order so that each lane ends up holding
+//     8 consecutive tokens, which is exactly the B-operand slice of P^T for the value
+//     product O^T = V^T P^T; V is stored feature-major, so its A operand is again one
+//     128-bit load per lane and P never leaves registers.
+// Rows: query row j < gs * s_q of a group is (i = j / gs, head = g * gs + j % gs);
+// rows beyond gs * s_q (up to the 16 of an MFMA tile) carry zero queries.
+#include "device_common.h"
+#include "gqla_internal.h"
+#include "tuned.h"
+
+#include <cmath>
+
+namespace gqla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ bf16x8 load8(const bf16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+__device__ __forceinline__ float xor_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  return fmaxf(v, __shfl_xor(v, 32, 64));
+}
+__device__ __forceinline__ float xor_sum(float v) {
+  v += __shfl_xor(v, 16, 64);
+  return v + __shfl_xor(v, 32, 64);
+}
+
+template <int DQK, int DV>
+__global__ __launch_bounds__(kWaves * 64, 2) void gqa_decode_split(AttnParams p) {
+  constexpr int KS = DQK / 32;     // k-steps of the score product
+  constexpr int NT = DV / 16;      // feature tiles of the value product
+  constexpr int CHUNK = kBlock * (DQK + DV);
+  __shared__ float s_o[kWaves][NT][64][4];   // per-wave O^T fragments (lane-major)
+  __shared__ float s_m[kWaves][16];
+  __shared__ float s_l[kWaves][16];
+  __shared__ int s_bad[kWaves];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15;          // query row owned by this lane (MFMA column)
+  const int grp = lane >> 4;          // k-group of the MFMA operands
+  const int split = blockIdx.x % p.n_split;
+  const int bg = blockIdx.x / p.n_split;
+  const int g = bg % p.kv_heads;
+  const int b = bg / p.kv_heads;
+  const int gs = p.heads_per_kv;
+  const int rows = gs * p.s_q;
+
+  const int L = p.ctx_lens[b];
+  const int nblk = (L + kBlock - 1) / kBlock;
+  bool bad = (L < p.s_q) || (L > p.max_blocks * kBlock) || (nblk > p.n_split * p.blocks_per_split);
+
+  // This lane's query row and its visible-token limit.
+  const int qi = col / gs;
+  const int qh = g * gs + col % gs;
+  const bool live_row = col < rows;
+  const int n_vis = live_row ? L - p.s_q + 1 + qi : L;
+
+  // B operand of S^T: Q^T slice (features 32*ks + 8*grp .. +8 of query row `col`).
+  bf16x8 qf[KS];
+  {
+    const bf16_t* q = static_cast<const bf16_t*>(p.q) +
+                      (static_cast<int64_t>(b * p.s_q + qi) * p.H + qh) * DQK + 8 * grp;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (live_row) qf[ks] = load8(q + 32 * ks);
+      else qf[ks] = bf16x8{};
+    }
+  }
+
+  f32x4 acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;   // running max, log2 domain
+  float l_run = 0.f;         // running sum over this lane's tokens
+  const float qk_scale = p.scale * kLog2e;
+
+  const bf16_t* kv = static_cast<const bf16_t*>(p.kv);
+  const int32_t* table = p.block_table + static_cast<int64_t>(b) * p.max_blocks;
+  const int blk_lo = split * p.blocks_per_split;
+  const int blk_hi = bad ? blk_lo : min(nblk, blk_lo + p.blocks_per_split);
+
+  for (int blk = blk_lo + wave; blk < blk_hi; blk += kWaves) {
+    const int32_t id = table[blk];
+    if (id < 0 || id >= p.num_blocks) { bad = true; break; }
+    const bf16_t* chunk = kv + (static_cast<int64_t>(id) * p.kv_heads + g) * CHUNK;
+    const bf16_t* vt = chunk + kBlock * DQK;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int t0 = half * 32;
+      // K rows for the two 16-token tiles, permuted so lane group `grp` gets tokens
+      // t0 + 8*grp .. +8 of this half.
+      bf16x8 kf[2][KS];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int tok = t0 + 8 * (col >> 2) + 4 * tt + (col & 3);
+        const bf16_t* krow = chunk + tok * DQK + 8 * grp;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kf[tt][ks] = load8(krow + 32 * ks);
+      }
+      bf16x8 vf[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) vf[nt] = load8(vt + (16 * nt + col) * kBlock + t0 + 8 * grp);
+
+      f32x4 s[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[tt][ks], qf[ks], s[tt], 0, 0, 0);
+      }
+      // Token of score s[tt][k] in this lane: blk*64 + t0 + 8*grp + 4*tt + k.
+      const int tbase = blk * kBlock + t0 + 8 * grp;
+      float sc[8];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float v = (tbase + 4 * tt + k < n_vis) ? s[tt][k] * qk_scale : -INFINITY;
+          sc[4 * tt + k] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = xor_max(mx);
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      m_run = m_new;
+      float psum = 0.f;
+      bf16x8 pf;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float e = __builtin_amdgcn_exp2f(sc[k] - m_use);
+        psum += e;
+        pf[k] = static_cast<__bf16>(e);
+      }
+      l_run = l_run * alpha + psum;
+      // Slots past the context hold arbitrary bits: zero those value columns.
+      if (blk * kBlock + t0 + 32 > L) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if (tbase + k >= L) vf[nt][k] = static_cast<__bf16>(0.f);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        acc[nt] *= alpha;
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[nt], pf, acc[nt], 0, 0, 0);
+      }
+    }
+  }
+
+  // Merge the four waves: O = sum_w 2^(m_w - M) O_w, l = sum_w 2^(m_w - M) l_w.
+  l_run = xor_sum(l_run);
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+    *reinterpret_cast<f32x4*>(&s_o[wave][nt][lane][0]) = acc[nt];
+  if (grp == 0) { s_m[wave][col] = m_run; s_l[wave][col] = l_run; }
+  if (lane == 0) s_bad[wave] = bad;
+  __syncthreads();
+
+  bool any_bad = false;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) any_bad |= s_bad[w] != 0;
+  // 256 threads: thread -> (query row jr, 8 consecutive features).
+  const int jr = threadIdx.x >> 4;
+  const int f0 = (threadIdx.x & 15) * 8;
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][jr]);
+  const float M_use = (M == -INFINITY) ? 0.f : M;
+  float wgt[kWaves];
+  float l_tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    wgt[w] = __builtin_amdgcn_exp2f(s_m[w][jr] - M_use);
+    l_tot += wgt[w] * s_l[w][jr];
+  }
+  float o[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    // feature f = f0 + k lives in tile f/16, lane (jr + 16 * ((f % 16) / 4)), slot f % 4
+    const int f = f0 + k;
+    const int ln = jr + 16 * ((f & 15) >> 2);
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) v += wgt[w] * s_o[w][f >> 4][ln][f & 3];
+    o[k] = v;
+  }
+  if (jr >= rows) return;
+  const int i = jr / gs;
+  const int h = g * gs + jr % gs;
+  const int64_t row = static_cast<int64_t>(b * p.s_q + i) * p.H + h;
+  if (p.n_split == 1) {
+    const float inv = 1.f / l_tot;
+    bf16_t packed[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) packed[k] = any_bad ? 0x7fc0 : f32_to_bf16(o[k] * inv);
+    *reinterpret_cast<uint4*>(static_cast<bf16_t*>(p.out) + row * DV + f0) = *reinterpret_cast<uint4*>(packed);
+    if (p.lse != nullptr && f0 == 0) p.lse[row] = any_bad ? nan_f32() : (M + __log2f(l_tot)) * kLn2;
+  } else {
+    const int64_t slot = row * p.n_split + split;
+    const bool empty = !(l_tot > 0.f);
+    float* dst = p.ws_o + slot * DV + f0;
+#pragma unroll
+    for (int k = 0; k < 8; k += 4) {
+      f32x4 v;
+      for (int u = 0; u < 4; ++u) v[u] = any_bad ? nan_f32() : (empty ? 0.f : o[k + u] / l_tot);
+      *reinterpret_cast<f32x4*>(dst + k) = v;
+    }
+    if (f0 == 0) p.ws_lse[slot] = any_bad ? nan_f32() : (empty ? -INFINITY : (M + __log2f(l_tot)) * kLn2);
+  }
+}
+
+}  // namespace
+
+bool tuned_gqa_supported(const gqla_dims* d) {
+  const int dqk = d->nope_dim + d->rope_dim;
+  const int gs = d->num_heads / d->num_groups;
+  return d->dtype == GQLA_BF16 && (dqk == 128 || dqk == 192) && d->v_dim == 128 && gs * d->s_q <= 16;
+}
+
+int tuned_gqa_target_wgs() { return 4 * kNumCUs; }
+int tuned_gqa_min_blocks_per_split() { return kWaves; }
+
+hipError_t launch_tuned_gqa(const AttnParams& p, const gqla_dims* d, hipStream_t s) {
+  const int64_t wgs = static_cast<int64_t>(p.B) * p.kv_heads * p.n_split;
+  if (wgs > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const int dqk = d->nope_dim + d->rope_dim;
+  if (dqk == 192) gqa_decode_split<192, 128><<<static_cast<unsigned>(wgs), kWaves * 64, 0, s>>>(p);
+  else gqa_decode_split<128, 128><<<static_cast<unsigned>(wgs), kWaves * 64, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace gqla

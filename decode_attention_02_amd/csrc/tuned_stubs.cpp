@@ -1,10 +1,6 @@
 // Placeholder: tuned kernels not yet built; every shape takes the generic kernels.
 #include "tuned.h"
 namespace gqla {
-bool tuned_gqa_supported(const gqla_dims*) { return false; }
-int tuned_gqa_target_wgs() { return 1024; }
-int tuned_gqa_min_blocks_per_split() { return 4; }
-hipError_t launch_tuned_gqa(const AttnParams&, const gqla_dims*, hipStream_t) { return hipErrorNotSupported; }
 bool tuned_absorb_supported(const gqla_dims*) { return false; }
 int tuned_absorb_target_wgs(const gqla_dims*) { return 256; }
 int tuned_absorb_min_blocks_per_split() { return 2; }

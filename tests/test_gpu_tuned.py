@@ -1,0 +1,83 @@
+"""GPU parity of the MFMA kernels at the production head shapes (bf16): ragged and
+one-token contexts, several split counts, shuffled block tables. Each case prints its
+name before it touches the GPU."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import gqla_ref as R
+from workloads import generate, workload
+
+from gpu_util import (TOL, Run, expanded_to_logical, log, logical_to_expanded, oracle_paths, rel_err,
+                      to_dev, to_host)
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [("llama3-8b-b32-ctx8k", 1), ("llama3-8b-b32-ctx8k", 2), ("dsv3-b64-ctx8k", 1),
+          ("dsv3-b64-ctx8k", 2), ("dsv3-tp8share-ctx16k", 2)]
+
+
+def _ctx(s_q):
+    return [s_q, 63, 64, 65, 129, 700]
+
+
+@pytest.mark.parametrize("name,s_q", SHAPES)
+@pytest.mark.parametrize("num_splits", [0, 1, 3])
+def test_gqa_decode_matches_oracle(name, s_q, num_splits):
+    w = workload(name)
+    x = generate(w, s_q, batch=6, ctx_lens=_ctx(s_q), shuffled=True, extra_blocks=3)
+    log(f"gqa {name} s_q={s_q} splits={num_splits}")
+    run = Run(x, num_splits)
+    got = run.gqa()
+    ref = oracle_paths(x)
+    for b in ref:
+        e = rel_err(got["out"][b], ref[b]["out"])
+        le = float(np.max(np.abs(got["lse"][b] - ref[b]["lse"])))
+        log(f"  seq {b} L={int(x.ctx_lens[b])}: out {e:.2e} lse_abs {le:.2e}")
+        assert e <= TOL["bf16"] and le <= TOL["bf16"] * max(1.0, float(np.max(np.abs(ref[b]["lse"]))))
+
+
+@pytest.mark.parametrize("name,s_q", [("dsv3-b64-ctx8k", 2), ("llama3-8b-b32-ctx8k", 2)])
+def test_gqa_decode_on_oracle_expanded_cache(name, s_q):
+    """Decode over an expanded cache built by the oracle (rounded to bf16), so the decode
+    kernel is checked on its own."""
+    from workloads import f64_to_bf16_bits
+    w = workload(name)
+    x = generate(w, s_q, batch=3, ctx_lens=[s_q, 200, 64], shuffled=True)
+    cache = x.f64(x.latent_cache)
+    K, V = R.expand_blocks(np.nan_to_num(cache), np.arange(x.num_blocks), x.f64(x.w_uk), x.f64(x.w_uv), w.latent)
+    flat = f64_to_bf16_bits(logical_to_expanded(K, V))
+    log(f"gqa-on-oracle-cache {name} s_q={s_q}")
+    run = Run(x)
+    got = run.gqa(expanded=to_dev(flat, "bf16"))
+    ref = oracle_paths(x)
+    for b in ref:
+        assert rel_err(got["out"][b], ref[b]["out"]) <= TOL["bf16"]
+
+
+def test_gqa_one_token_context_is_value_row():
+    """A one-token context returns that token's expanded value row: bf16 in, bf16 out,
+    so the GPU output equals the expanded cache entry bit for bit."""
+    w = workload("dsv3-b64-ctx8k")
+    x = generate(w, 1, batch=2, ctx_lens=[1, 1], shuffled=True)
+    log("gqa one-token")
+    run = Run(x)
+    expanded = run.expand()
+    got = run.gqa(expanded)
+    _, V = expanded_to_logical(to_host(expanded), x.num_blocks, w.groups, w.qk, w.v)
+    for b in range(2):
+        blk = x.block_table[b, 0]
+        for h in range(w.heads):
+            g = h // w.group_size
+            assert np.array_equal(got["out"][b, 0, h], V[blk, g, 0]), (b, h)
+
+
+@pytest.mark.parametrize("name,s_q", SHAPES)
+def test_paths_agree_on_gpu(name, s_q):
+    w = workload(name)
+    x = generate(w, s_q, batch=3, ctx_lens=[s_q, 333, 1000], shuffled=True)
+    log(f"absorb-vs-gqa {name} s_q={s_q}")
+    run = Run(x)
+    a, g = run.absorb()["out"], run.gqa()["out"]
+    for b in range(3):
+        assert rel_err(a[b], g[b]) <= TOL["bf16"]

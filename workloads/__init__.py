@@ -10,6 +10,7 @@ from .shapes import WORKLOADS, Workload, workload
 from .generate import (
     Inputs,
     generate,
+    queries_for,
     bf16_bits_to_f64,
     f64_to_bf16_bits,
     rope_rotate,
@@ -21,6 +22,7 @@ __all__ = [
     "workload",
     "Inputs",
     "generate",
+    "queries_for",
     "bf16_bits_to_f64",
     "f64_to_bf16_bits",
     "rope_rotate",

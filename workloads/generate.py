@@ -162,11 +162,24 @@ def generate(w: Workload, s_q: int, *, batch: Optional[int] = None,
     std = 1.0 / np.sqrt(dc)
     w_uk = _store(np.random.default_rng(ss_wk).standard_normal((G, dn, dc)) * std, dt)
     w_uv = _store(np.random.default_rng(ss_wv).standard_normal((G, dv, dc)) * std, dt)
-    q_nope = np.random.default_rng(ss_qn).standard_normal((B, s_q, H, dn))
-    q_rope = np.random.default_rng(ss_qr).standard_normal((B, s_q, H, dr))
-    pos = lens[:, None] - s_q + np.arange(s_q)[None, :]          # [B][s_q]
-    q_rope = rope_rotate(q_rope, pos[:, :, None])
+    q_nope, q_rope = _queries(w, s_q, lens, ss_qn, ss_qr, dt)
     return Inputs(w=w, s_q=s_q, dtype=dt, ctx_lens=lens.astype(np.int32),
                   block_table=table, num_blocks=num_blocks, latent_cache=cache,
-                  w_uk=w_uk, w_uv=w_uv, q_nope=_store(q_nope, dt), q_rope=_store(q_rope, dt),
+                  w_uk=w_uk, w_uv=w_uv, q_nope=q_nope, q_rope=q_rope,
                   c_kv_seq=c_seq, k_rope_seq=r_seq)
+
+
+def _queries(w: Workload, s_q: int, lens: np.ndarray, ss_qn, ss_qr, dt: str):
+    B, H = len(lens), w.heads
+    q_nope = np.random.default_rng(ss_qn).standard_normal((B, s_q, H, w.nope))
+    q_rope = np.random.default_rng(ss_qr).standard_normal((B, s_q, H, w.rope))
+    pos = np.asarray(lens)[:, None] - s_q + np.arange(s_q)[None, :]   # [B][s_q]
+    q_rope = rope_rotate(q_rope, pos[:, :, None])
+    return _store(q_nope, dt), _store(q_rope, dt)
+
+
+def queries_for(x: Inputs, s_q: int, seed: Optional[int] = None):
+    """Queries of batch x at another s_q (same seed streams, same context lengths):
+    returns (q_nope, q_rope) in the storage dtype."""
+    streams = np.random.SeedSequence(x.w.seed if seed is None else seed).spawn(8)
+    return _queries(x.w, s_q, x.ctx_lens.astype(np.int64), streams[4], streams[5], x.dtype)
