@@ -1,0 +1,458 @@
+// MQA-absorb split-KV decode on gfx950 MFMA (bf16 latent, fp32 accumulation).
+//
+// Every query head, with W_UK^g folded into it, attends over the one shared latent
+// "key head" [c_KV | k_rope] and takes the latent c_KV itself as its value (MLA's
+// absorbed form, which GQLA keeps unchanged: "GQLA: Attention latente ...", English
+// abstract; gqla_attn.py docstring: a single MQA-style head per layer).
+//
+// All H * s_q query rows of a sequence read the same 64-token latent tiles, so the
+// tile is fetched from HBM once per workgroup and shared through LDS:
+//   * tiles (64 tokens x 576 bf16 = 72 KiB) are copied global -> LDS by
+//     global_load_lds_dwordx4 (no register staging), double-buffered, with an XOR
+//     swizzle of the 16-byte chunks inside each 128-byte group so that both LDS
+//     access patterns below are bank-conflict free;
+//   * each wave owns 16 query rows (one MFMA tile): scores S^T = C Q^T
+//     (v_mfma_f32_16x16x32_bf16, A = 16 tokens x 32 latent features read with
+//     ds_read_b128, B = the wave's absorbed queries held in registers);
+//   * the value product O^T = C^T P^T needs the latent with tokens along the
+//     contraction, which ds_read_b64_tr_b16 delivers directly from the row-major tile;
+//     P stays in registers as the B operand;
+//   * small row counts (16 or 32 rows) also split each tile's two 32-token halves
+//     over two waves, merged at the end, so a workgroup still has 4 waves streaming;
+//   * more than 128 rows use two workgroups per (sequence, split), placed on the same
+//     XCD so the second tile read is served from that XCD's L2.
+#include "device_common.h"
+#include "gqla_internal.h"
+#include "tuned.h"
+
+#include <cmath>
+
+namespace gqla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kDC = 512;                 // latent rank
+constexpr int kDQ = 576;                 // latent + RoPE values per token
+constexpr int kRowBytes = kDQ * 2;       // 1152
+constexpr int kChunks = kDQ / 8;         // 16-byte chunks per token row (72)
+constexpr int kTileBytes = kBlock * kRowBytes;  // 73728
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Swizzle of a token row's 16-byte chunk index inside its 128-byte group.
+__device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+__device__ __forceinline__ int chunk_off(int t, int c) {
+  return t * kRowBytes + (((c & ~7) | ((c & 7) ^ swz(t))) << 4);
+}
+
+__device__ __forceinline__ float xor_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  return fmaxf(v, __shfl_xor(v, 32, 64));
+}
+__device__ __forceinline__ float xor_sum(float v) {
+  v += __shfl_xor(v, 16, 64);
+  return v + __shfl_xor(v, 32, 64);
+}
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt low bits [3:0], high
+// bits [15:14]; expcnt and lgkmcnt fields left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+}
+
+__device__ __forceinline__ void lds_barrier() {
+  // Workgroup barrier without the memory fence of __syncthreads(): the fence would
+  // also wait for the next tile's copy, which must stay in flight. Callers wait for
+  // exactly the counters they need first.
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+constexpr int kMaxSplitBlocks = 2048;    // block ids of one split staged in LDS
+constexpr float kRescaleSlack = 8.f;     // log2 headroom before the accumulator is rescaled
+
+// The two tile buffers are distinct LDS objects so that the compiler can see that a
+// copy into one never aliases reads of the other, and keeps the copy in flight.
+__shared__ __attribute__((aligned(16))) char g_tile0[kTileBytes];
+__shared__ __attribute__((aligned(16))) char g_tile1[kTileBytes];
+__shared__ int32_t g_ids[kMaxSplitBlocks];
+
+template <int BUF>
+__device__ __forceinline__ char* tile_buf() { return BUF == 0 ? g_tile0 : g_tile1; }
+
+// RPW = 16-row tiles per wave (1 or 2; two tiles share every LDS operand read),
+// RT = row tiles per workgroup, TG = waves splitting each tile's two 32-token halves.
+template <int RPW, int RT, int TG>
+struct AbsorbCta {
+  static constexpr int WR = RT / RPW;                          // waves along rows
+  static constexpr int W = WR * TG;
+  static constexpr int PER_WAVE = kChunks * kBlock / 64 / W;   // 1 KiB copies per wave per tile
+  static_assert(PER_WAVE * W * 64 == kChunks * kBlock, "tile must split evenly over waves");
+  static constexpr int FT = kDC / 16;                          // feature tiles of O^T
+  static constexpr int KS = kDQ / 32;                          // k-steps of the score product
+
+  const AttnParams& p;
+  int lane, wave, wr, tg, col, grp;
+  int b, split, L, blk_lo, nb;
+  bool bad;
+  int qi[RPW], qh[RPW], n_vis[RPW];
+  bf16x8 qf[RPW][KS];
+  f32x4 acc[RPW][FT];
+  float m_ref[RPW], l_run[RPW];
+  float qk_scale;
+  // per-lane LDS byte offsets (see score() and value())
+  int s_base_even, s_base_odd;
+  int v_base[4];
+
+  __device__ AbsorbCta(const AttnParams& p_) : p(p_) {}
+
+  // Copy the tile of the k-th block of the split into buffer BUF. Wave instruction j
+  // writes LDS slots (wave * PER_WAVE + j) * 64 + lane, each a 16-byte chunk; the lane
+  // fetches the logical chunk that the swizzle stores at its slot.
+  template <int BUF>
+  __device__ __forceinline__ void issue(int k) {
+    const int32_t id = max(g_ids[k], 0);   // invalid ids already poisoned the output
+    const char* src = static_cast<const char*>(p.kv) + static_cast<int64_t>(id) * kTileBytes;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));           // recompute offsets here instead of holding them
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int slot = (wave * PER_WAVE + j) * 64 + ln;
+      const int t = slot / kChunks, cp = slot - t * kChunks;
+      const int c = (cp & ~7) | ((cp & 7) ^ swz(t));
+      __builtin_amdgcn_global_load_lds(src + (t * kRowBytes + c * 16),
+                                       (lds_void*)(tile_buf<BUF>() + (wave * PER_WAVE + j) * 1024), 16, 0, 0);
+    }
+  }
+
+  // Scores S^T = C Q^T of the 32 tokens t0 .. t0+31 for each row tile of the wave.
+  // Chunk 4*ks + grp of token row `tok` sits at tok*1152 + 16*(...) per the swizzle;
+  // since tok = t0 + 16*tt + col with t0 + 16*tt a multiple of 8, swz(tok) = swz(col)
+  // and the address is a per-lane base (even or odd ks) plus a compile-time offset.
+  template <int BUF>
+  __device__ __forceinline__ void score(int t0, f32x4 (&s)[RPW][2]) {
+    const char* tile = tile_buf<BUF>() + t0 * kRowBytes;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) s[r][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      auto ld = [&](int ks) {
+        return *reinterpret_cast<const bf16x8*>(tile + tt * 16 * kRowBytes + ((ks & 1) ? s_base_odd : s_base_even) +
+                                                128 * (ks >> 1));
+      };
+      bf16x8 a0 = ld(0), a1 = ld(1);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        bf16x8 a2 = a1;
+        if (ks + 2 < KS) a2 = ld(ks + 2);
+#pragma unroll
+        for (int r = 0; r < RPW; ++r)
+          s[r][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[r][ks], s[r][tt], 0, 0, 0);
+        a0 = a1;
+        a1 = a2;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  // O^T += C^T P^T over the 32 tokens t0 .. t0+31: lane (feature f, group grp) needs the
+  // latent of tokens t0 + 4*grp + {0..3} and t0 + 16 + 4*grp + {0..3}; each 16-lane group
+  // feeds ds_read_b64_tr_b16 with 4 features 4*(col&3) of token row col>>2. Per-lane
+  // bases exist for the four values of ft & 3; the rest is a compile-time offset.
+  template <int BUF>
+  __device__ __forceinline__ void value(int t0, const bf16x8 (&pf)[RPW], int tb, bool last) {
+    const char* tile = tile_buf<BUF>() + t0 * kRowBytes;
+    auto tr = [&](int ft, int second) {
+      return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(tile + v_base[ft & 3] + 128 * (ft >> 2) + second * 16 * kRowBytes));
+    };
+    i16x4 lo0 = tr(0, 0), hi0 = tr(0, 1), lo1 = tr(1, 0), hi1 = tr(1, 1);
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) {
+      i16x4 lo2 = lo1, hi2 = hi1;
+      if (ft + 2 < FT) { lo2 = tr(ft + 2, 0); hi2 = tr(ft + 2, 1); }
+      if (last) {   // slots past the context hold arbitrary bits
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (tb + e >= L) lo0[e] = 0;
+          if (tb + 16 + e >= L) hi0[e] = 0;
+        }
+      }
+      const i16x8 av = __builtin_shufflevector(lo0, hi0, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int r = 0; r < RPW; ++r)
+        acc[r][ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), pf[r], acc[r][ft], 0, 0, 0);
+      lo0 = lo1; hi0 = hi1;
+      lo1 = lo2; hi1 = hi2;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // Online softmax of one 32-token step for row tile r; returns P^T as the B operand.
+  __device__ __forceinline__ bf16x8 softmax(int r, const f32x4 (&sr)[2], int tb) {
+    float sc[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2) {
+        const float v = (tb + 16 * tt + k2 < n_vis[r]) ? sr[tt][k2] * qk_scale : -INFINITY;
+        sc[4 * tt + k2] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = xor_max(mx);
+    const bool grow = mx > m_ref[r] + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // wave-uniform, rare after the first block
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref[r] - mx) : 1.f;
+      if (grow) m_ref[r] = mx;
+      l_run[r] *= alpha;
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft) acc[r][ft] *= alpha;
+    }
+    const float m_use = (m_ref[r] == -INFINITY) ? 0.f : m_ref[r];
+    float psum = 0.f;
+    bf16x8 pf;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float e = __builtin_amdgcn_exp2f(sc[j] - m_use);
+      psum += e;
+      pf[j] = static_cast<__bf16>(e);
+    }
+    l_run[r] += psum;
+    return pf;
+  }
+
+  // One 64-token block held in buffer BUF (k-th block of the split), with the copy of
+  // block k + 1 into the other buffer issued first.
+  // One 64-token block slot held in buffer BUF: first issue the copy of the next block
+  // (clamped to the last one, a re-read that hits L2) into the other buffer, so every
+  // step issues the same copies and the compiler can track which buffer each LDS read
+  // depends on; slots past the split's last block only keep that rhythm.
+  template <int BUF>
+  __device__ __forceinline__ void step(int k) {
+    issue<1 - BUF>(min(k + 1, nb - 1));
+    wait_vmcnt<PER_WAVE>();
+    lds_barrier();
+    if (k < nb) {
+      const int blk = blk_lo + k;
+      const bool last = (blk + 1) * kBlock > L;
+      auto half_step = [&](int hh) {
+        const int t0 = hh * 32;
+        f32x4 s[RPW][2];
+        score<BUF>(t0, s);
+        const int tb = blk * kBlock + t0 + 4 * grp;
+        bf16x8 pf[RPW];
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) pf[r] = softmax(r, s[r], tb);
+        value<BUF>(t0, pf, tb, last);
+      };
+      if (TG == 2) {
+        half_step(tg);
+      } else {
+        half_step(0);
+        half_step(1);
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    lds_barrier();
+  }
+
+  __device__ __forceinline__ void run(int unit, int part) {
+    lane = threadIdx.x & 63;
+    wave = threadIdx.x >> 6;
+    wr = wave % WR;
+    tg = wave / WR;
+    col = lane & 15;
+    grp = lane >> 4;
+    split = unit % p.n_split;
+    b = unit / p.n_split;
+    L = p.ctx_lens[b];
+    const int nblk = (L + kBlock - 1) / kBlock;
+    bad = (L < p.s_q) || (L > p.max_blocks * kBlock) || (nblk > p.n_split * p.blocks_per_split);
+    blk_lo = split * p.blocks_per_split;
+    const int blk_hi = bad ? blk_lo : min(nblk, blk_lo + p.blocks_per_split);
+    nb = max(0, blk_hi - blk_lo);
+
+    // Stage this split's block ids in LDS; -1 marks an id outside the pool.
+    {
+      const int32_t* table = p.block_table + static_cast<int64_t>(b) * p.max_blocks + blk_lo;
+      for (int i = threadIdx.x; i < nb; i += W * 64) {
+        const int32_t id = table[i];
+        g_ids[i] = (id < 0 || id >= p.num_blocks) ? -1 : id;
+      }
+    }
+
+    // Rows of this lane, one per row tile r: row = (part * RT + wr * RPW + r) * 16 + col,
+    // i.e. query row i = row / H of head h = row % H.
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int row = (part * RT + wr * RPW + r) * 16 + col;
+      qi[r] = row / p.H;
+      qh[r] = row % p.H;
+      n_vis[r] = L - p.s_q + 1 + qi[r];
+      const bf16_t* q = static_cast<const bf16_t*>(p.q) +
+                        (static_cast<int64_t>(b * p.s_q + qi[r]) * p.H + qh[r]) * kDQ + 8 * grp;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[r][ks] = *reinterpret_cast<const bf16x8*>(q + 32 * ks);
+      m_ref[r] = -INFINITY;
+      l_run[r] = 0.f;
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft) acc[r][ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    qk_scale = p.scale * kLog2e;
+    {
+      const int sw = swz(col);
+      const int lo2 = (grp ^ sw) & 3;
+      s_base_even = col * kRowBytes + 16 * ((0 ^ (sw & 4)) | lo2);
+      s_base_odd = col * kRowBytes + 16 * ((4 ^ (sw & 4)) | lo2);
+      const int src = 4 * grp + (col >> 2);    // token row fed by this lane (relative to t0)
+      const int sw2 = swz(src);
+      const int m4 = col & 3;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        v_base[q4] = src * kRowBytes + 16 * ((2 * q4 + (m4 >> 1)) ^ sw2) + 8 * (m4 & 1);
+    }
+
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    lds_barrier();
+    for (int i = 0; i < nb; ++i) bad |= g_ids[i] < 0;   // uniform: every lane reads all ids
+    const int nb_run = bad ? 0 : nb;
+    nb = nb_run;
+    // Blocks alternate buffers 0 and 1 in pairs.
+    if (nb > 0) {
+      issue<0>(0);
+      for (int k = 0; k < nb; k += 2) {
+        step<0>(k);
+        step<1>(k + 1);
+      }
+      wait_vmcnt<0>();
+      lds_barrier();   // every wave's last copy has landed before LDS is reused below
+    }
+
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) l_run[r] = xor_sum(l_run[r]);
+    if (TG == 2) {   // merge the two token halves of each row tile through LDS
+      float* xo = reinterpret_cast<float*>(g_tile0);        // [WR][RPW][FT][64 lanes][4]
+      float* xm = reinterpret_cast<float*>(g_tile1);        // [WR][RPW][64]
+      float* xl = xm + WR * RPW * 64;
+      if (tg == 1) {
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+#pragma unroll
+          for (int ft = 0; ft < FT; ++ft)
+            *reinterpret_cast<f32x4*>(xo + (((wr * RPW + r) * FT + ft) * 64 + lane) * 4) = acc[r][ft];
+          xm[(wr * RPW + r) * 64 + lane] = m_ref[r];
+          xl[(wr * RPW + r) * 64 + lane] = l_run[r];
+        }
+      }
+      __syncthreads();
+      if (tg == 1) return;
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        const float m1 = xm[(wr * RPW + r) * 64 + lane], l1 = xl[(wr * RPW + r) * 64 + lane];
+        const float M = fmaxf(m_ref[r], m1);
+        const float M_use = (M == -INFINITY) ? 0.f : M;
+        const float w0 = __builtin_amdgcn_exp2f(m_ref[r] - M_use), w1 = __builtin_amdgcn_exp2f(m1 - M_use);
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft) {
+          const f32x4 o1 = *reinterpret_cast<const f32x4*>(xo + (((wr * RPW + r) * FT + ft) * 64 + lane) * 4);
+          acc[r][ft] = acc[r][ft] * w0 + o1 * w1;
+        }
+        l_run[r] = l_run[r] * w0 + l1 * w1;
+        m_ref[r] = M;
+      }
+    }
+    store();
+  }
+
+  __device__ __forceinline__ void store() {
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int64_t orow = static_cast<int64_t>(b * p.s_q + qi[r]) * p.H + qh[r];
+      const bool empty = !(l_run[r] > 0.f);
+      const float inv = empty ? 0.f : 1.f / l_run[r];
+      float* dst = (p.n_split == 1 ? static_cast<float*>(p.out) + orow * kDC
+                                   : p.ws_o + (orow * p.n_split + split) * kDC) + 4 * grp;
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft) {
+        f32x4 v = acc[r][ft] * inv;
+        if (bad) v = f32x4{nan_f32(), nan_f32(), nan_f32(), nan_f32()};
+        *reinterpret_cast<f32x4*>(dst + 16 * ft) = v;
+      }
+      if (grp == 0) {
+        const float lse = bad ? nan_f32() : (empty ? -INFINITY : (m_ref[r] + __log2f(l_run[r])) * kLn2);
+        if (p.n_split == 1) {
+          if (p.lse != nullptr) p.lse[orow] = lse;
+        } else {
+          p.ws_lse[orow * p.n_split + split] = lse;
+        }
+      }
+    }
+  }
+};
+
+// The H * s_q rows of a sequence are split into `parts` workgroups of RT * 16 rows. The
+// parts of one (sequence, split) unit get workgroup ids 8 apart, which the dispatcher
+// places on the same XCD, so each latent tile is read from HBM once and from that
+// XCD's L2 by the other parts.
+template <int RPW, int RT, int TG>
+__global__ __launch_bounds__(RT / RPW * TG * 64, 1) void absorb_decode_split(AttnParams p, int parts, int units) {
+  const int x = blockIdx.x & 7, y = blockIdx.x >> 3;
+  const int unit = parts == 1 ? static_cast<int>(blockIdx.x) : (y / parts) * 8 + x;
+  const int part = parts == 1 ? 0 : y % parts;
+  if (unit >= units) return;
+  AbsorbCta<RPW, RT, TG> cta(p);
+  cta.run(unit, part);
+}
+
+template <int RPW, int RT, int TG>
+hipError_t launch(const AttnParams& p, int parts, hipStream_t s) {
+  if (p.blocks_per_split > kMaxSplitBlocks) return hipErrorInvalidValue;
+  const int64_t units = static_cast<int64_t>(p.B) * p.n_split;
+  const int64_t grid = parts == 1 ? units : ((units * parts + 8 * parts - 1) / (8 * parts)) * (8 * parts);
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  absorb_decode_split<RPW, RT, TG><<<static_cast<unsigned>(grid), RT / RPW * TG * 64, 0, s>>>(p, parts, static_cast<int>(units));
+  return hipGetLastError();
+}
+
+int absorb_parts(const gqla_dims* d) {
+  const int rows = d->num_heads * d->s_q;
+  return rows > 64 ? rows / 64 : 1;
+}
+
+}  // namespace
+
+bool tuned_absorb_supported(const gqla_dims* d) {
+  const int rows = d->num_heads * d->s_q;
+  return d->dtype == GQLA_BF16 && d->latent_rank == kDC && d->rope_dim == kDQ - kDC &&
+         (rows == 16 || rows == 32 || rows == 64 || rows == 128 || rows == 256);
+}
+
+// One 156 KiB workgroup per CU; each (sequence, split) unit takes absorb_parts() of them.
+int tuned_absorb_target_wgs(const gqla_dims* d) { return kNumCUs / absorb_parts(d); }
+
+int tuned_absorb_min_blocks_per_split() { return 4; }
+
+int tuned_absorb_max_blocks_per_split() { return kMaxSplitBlocks; }
+
+hipError_t launch_tuned_absorb(const AttnParams& p, const gqla_dims* d, hipStream_t s) {
+  switch (d->num_heads * d->s_q) {
+    case 16: return launch<1, 1, 2>(p, 1, s);
+    case 32: return launch<1, 2, 2>(p, 1, s);
+    case 64: return launch<1, 4, 1>(p, 1, s);
+    case 128: return launch<1, 4, 1>(p, 2, s);
+    case 256: return launch<1, 4, 1>(p, 4, s);
+  }
+  return hipErrorNotSupported;
+}
+
+}  // namespace gqla

@@ -103,6 +103,8 @@ Plan plan(const gqla_dims* d, const gqla_paged* p, int32_t path) {
   }
   if (p->num_splits > 0) n = p->num_splits;
   n = std::max(1, std::min(n, std::min(nblk, 1024)));
+  if (path == GQLA_PATH_ABSORB && pl.tuned)   // the kernel stages one split's block ids in LDS
+    n = std::max(n, (nblk + gqla::tuned_absorb_max_blocks_per_split() - 1) / gqla::tuned_absorb_max_blocks_per_split());
   pl.blocks_per_split = (nblk + n - 1) / n;
   pl.n_split = (nblk + pl.blocks_per_split - 1) / pl.blocks_per_split;
   return pl;

@@ -16,6 +16,7 @@ hipError_t launch_tuned_gqa(const AttnParams& p, const gqla_dims* d, hipStream_t
 bool tuned_absorb_supported(const gqla_dims* d);
 int tuned_absorb_target_wgs(const gqla_dims* d);
 int tuned_absorb_min_blocks_per_split();
+int tuned_absorb_max_blocks_per_split();
 hipError_t launch_tuned_absorb(const AttnParams& p, const gqla_dims* d, hipStream_t s);
 
 bool tuned_absorb_query_supported(const gqla_dims* d);

@@ -81,3 +81,40 @@ def test_paths_agree_on_gpu(name, s_q):
     a, g = run.absorb()["out"], run.gqa()["out"]
     for b in range(3):
         assert rel_err(a[b], g[b]) <= TOL["bf16"]
+
+
+ABSORB_SHAPES = [("llama3-8b-b32-ctx8k", 1), ("llama3-8b-b32-ctx8k", 2), ("dsv3-b64-ctx8k", 1),
+                 ("dsv3-b64-ctx8k", 2), ("dsv3-tp8share-ctx16k", 1), ("dsv3-tp8share-ctx16k", 2)]
+
+
+@pytest.mark.parametrize("name,s_q", ABSORB_SHAPES)
+@pytest.mark.parametrize("num_splits", [0, 1, 3])
+def test_absorb_path_matches_oracle(name, s_q, num_splits):
+    w = workload(name)
+    x = generate(w, s_q, batch=6, ctx_lens=_ctx(s_q), shuffled=True, extra_blocks=3)
+    log(f"absorb {name} s_q={s_q} splits={num_splits}")
+    run = Run(x, num_splits)
+    got = run.absorb()
+    ref = oracle_paths(x)
+    for b in ref:
+        r = ref[b]
+        e = dict(q_abs=rel_err(got["q_abs"][b], r["q_abs"]), o_lat=rel_err(got["o_lat"][b], r["o_lat"]),
+                 out=rel_err(got["out"][b], r["out"]))
+        le = float(np.max(np.abs(got["lse"][b] - r["lse"])))
+        log(f"  seq {b} L={int(x.ctx_lens[b])}: " + " ".join(f"{k} {v:.2e}" for k, v in e.items()) + f" lse_abs {le:.2e}")
+        for k, v in e.items():
+            assert v <= TOL["bf16"], (k, v)
+        assert le <= TOL["bf16"] * max(1.0, float(np.max(np.abs(r["lse"]))))
+
+
+def test_absorb_one_token_context_is_latent_row():
+    """With one visible token the absorb decode returns that token's latent row exactly
+    (fp32 o_lat of a bf16 value)."""
+    w = workload("dsv3-b64-ctx8k")
+    x = generate(w, 2, batch=2, ctx_lens=[2, 2], shuffled=True)
+    log("absorb one-token")
+    got = Run(x).absorb()
+    for b in range(2):
+        c0 = x.f64(x.c_kv_seq[b][0])
+        for h in range(w.heads):
+            assert np.array_equal(got["o_lat"][b, 0, h], c0), (b, h)
