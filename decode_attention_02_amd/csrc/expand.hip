@@ -1,0 +1,252 @@
+// Latent -> per-group K/V cache expansion on gfx950 MFMA (bf16, fp32 accumulation).
+//
+// GQLA's GQA path expands the cached latent into G full key/value heads ("GQLA:
+// Attention latente ...", English abstract; gqla_attn.py docstring, GQA path):
+//   K[p][g][r] = [ W_UK^g c_r ; kr_r ],  V[p][g][r] = W_UV^g c_r,
+// a GEMM of 64-token latent tiles against each group's stacked [W_UK^g ; W_UV^g]
+// (d_n + d_v rows by d_c = 512).
+//
+// A workgroup owns one group and a run of listed blocks. Each wave keeps a 32-row
+// slice of [W_UK^g ; W_UV^g] in registers for the whole run, so the weights are read
+// once per workgroup, while the latent tiles stream through LDS (global_load_lds,
+// double-buffered, the XOR-swizzled layout of the absorb decode). Key rows come out of
+// K^T = W_UK^g C^T, whose accumulator holds 4 consecutive key features of one token
+// (8-byte stores into the token-major K); value rows come out of V = C W_UV^g^T, whose
+// accumulator holds 4 consecutive tokens of one feature (8-byte stores into the
+// feature-major V). The RoPE key is copied into every group's K.
+#include "device_common.h"
+#include "gqla_internal.h"
+#include "tuned.h"
+
+#include <algorithm>
+
+namespace gqla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kDC = 512;
+constexpr int kDR = 64;
+constexpr int kDQ = kDC + kDR;
+constexpr int kRowBytes = kDQ * 2;
+constexpr int kChunks = kDQ / 8;
+constexpr int kTileBytes = kBlock * kRowBytes;
+constexpr int kDV = 128;
+
+__device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+}
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__shared__ __attribute__((aligned(16))) char e_tile0[kTileBytes];
+__shared__ __attribute__((aligned(16))) char e_tile1[kTileBytes];
+constexpr int kMaxRun = 2048;        // listed blocks per workgroup (ids staged in LDS)
+__shared__ int32_t e_ids[kMaxRun];
+
+template <int BUF>
+__device__ __forceinline__ char* etile() { return BUF == 0 ? e_tile0 : e_tile1; }
+
+// DN = nope dim (64 or 128); W = (DN + 128) / 32 waves, wave w owns stacked weight rows
+// 32w .. 32w+31 (key rows first, then value rows).
+template <int DN>
+struct ExpandCta {
+  static constexpr int DQK = DN + kDR;
+  static constexpr int W = (DN + kDV) / 32;
+  static constexpr int PER_WAVE = kChunks * kBlock / 64 / W;
+  static_assert(PER_WAVE * W * 64 == kChunks * kBlock, "tile must split evenly over waves");
+  static constexpr int KS = kDC / 32;
+
+  const ProjParams& d;
+  const bf16_t* latent;
+  const int32_t* ids;
+  int64_t num_blocks;
+  bf16_t* expanded;
+  int g, j0, nj;
+  int lane, wave, col, grp;
+  bool is_key;
+  int row0;                 // first weight row of this wave within its matrix
+  bf16x8 wf[2][KS];         // the wave's weight rows, MFMA operand layout
+  int base_even, base_odd;  // per-lane LDS offsets of the latent operand
+
+  __device__ ExpandCta(const ProjParams& d_, const bf16_t* lat, const int32_t* ids_, int64_t nb, bf16_t* ex)
+      : d(d_), latent(lat), ids(ids_), num_blocks(nb), expanded(ex) {}
+
+  // Ids staged in LDS (-1 = outside the pool, skipped), so fetching one never waits on
+  // the vector-memory counter that tracks the tile copies.
+  __device__ __forceinline__ int block_id(int j) const { return e_ids[j]; }
+
+  template <int BUF>
+  __device__ __forceinline__ void issue(int j) {
+    const int id = max(block_id(j), 0);   // skipped ids still copy a valid block
+    const char* src = reinterpret_cast<const char*>(latent) + static_cast<int64_t>(id) * kTileBytes;
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int k = 0; k < PER_WAVE; ++k) {
+      const int slot = (wave * PER_WAVE + k) * 64 + ln;
+      const int t = slot / kChunks, cp = slot - t * kChunks;
+      const int c = (cp & ~7) | ((cp & 7) ^ swz(t));
+      __builtin_amdgcn_global_load_lds(src + (t * kRowBytes + c * 16),
+                                       (lds_void*)(etile<BUF>() + (wave * PER_WAVE + k) * 1024), 16, 0, 0);
+    }
+  }
+
+  // Key rows (K^T = W C^T) or value rows (V = C W^T) of one 64-token tile; the
+  // orientation is a compile-time choice taken under a wave-uniform branch.
+  template <int BUF, bool KEY>
+  __device__ __forceinline__ void tiles(bf16_t* chunk) {
+    const char* tile = etile<BUF>();
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      const char* rows = tile + tt * 16 * kRowBytes;
+      auto ld = [&](int ks) {
+        return *reinterpret_cast<const bf16x8*>(rows + ((ks & 1) ? base_odd : base_even) + 128 * (ks >> 1));
+      };
+      bf16x8 a0 = ld(0), a1 = ld(1);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        bf16x8 a2 = a1;
+        if (ks + 2 < KS) a2 = ld(ks + 2);
+#pragma unroll
+        for (int ft = 0; ft < 2; ++ft) {
+          if (KEY) acc[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[ft][ks], a0, acc[ft], 0, 0, 0);
+          else acc[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, wf[ft][ks], acc[ft], 0, 0, 0);
+        }
+        a0 = a1;
+        a1 = a2;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int ft = 0; ft < 2; ++ft) {
+        bf16_t packed[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) packed[k] = f32_to_bf16(acc[ft][k]);
+        if (KEY) {
+          // K^T tile: lane = token tt*16 + col, key features row0 + 16*ft + 4*grp + k
+          const int tok = tt * 16 + col;
+          *reinterpret_cast<uint2*>(chunk + tok * DQK + row0 + 16 * ft + 4 * grp) = *reinterpret_cast<uint2*>(packed);
+        } else {
+          // V tile: lane = value feature row0 + 16*ft + col, tokens tt*16 + 4*grp + k
+          const int f = row0 + 16 * ft + col;
+          *reinterpret_cast<uint2*>(chunk + kBlock * DQK + f * kBlock + tt * 16 + 4 * grp) =
+              *reinterpret_cast<uint2*>(packed);
+        }
+      }
+    }
+  }
+
+  template <int BUF>
+  __device__ __forceinline__ void compute(int id) {
+    const char* tile = etile<BUF>();
+    bf16_t* chunk = expanded + (static_cast<int64_t>(id) * d.G + g) * kBlock * (DQK + kDV);
+    if (is_key) tiles<BUF, true>(chunk);
+    else tiles<BUF, false>(chunk);
+    // RoPE key copy: 64 tokens x 64 values, 16 bytes per lane-step over the workgroup.
+    for (int i = threadIdx.x; i < kBlock * kDR / 8; i += W * 64) {
+      const int tok = i / (kDR / 8), c = kDC / 8 + i % (kDR / 8);
+      const uint4 v = *reinterpret_cast<const uint4*>(tile + tok * kRowBytes + (((c & ~7) | ((c & 7) ^ swz(tok))) << 4));
+      *reinterpret_cast<uint4*>(chunk + tok * DQK + DN + 8 * (i % (kDR / 8))) = v;
+    }
+  }
+
+  template <int BUF>
+  __device__ __forceinline__ void step(int j) {
+    issue<1 - BUF>(min(j + 1, nj - 1));
+    wait_vmcnt<PER_WAVE>();
+    lds_barrier();
+    if (j < nj) {
+      const int id = block_id(j);
+      if (id >= 0) compute<BUF>(id);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    lds_barrier();
+  }
+
+  __device__ __forceinline__ void run(const bf16_t* w_uk, const bf16_t* w_uv, int j0_, int nj_, int g_) {
+    j0 = j0_;
+    nj = nj_;
+    g = g_;
+    lane = threadIdx.x & 63;
+    wave = threadIdx.x >> 6;
+    col = lane & 15;
+    grp = lane >> 4;
+    is_key = wave * 32 < DN;
+    row0 = is_key ? wave * 32 : wave * 32 - DN;
+    const bf16_t* wmat = is_key ? w_uk + static_cast<int64_t>(g) * DN * kDC : w_uv + static_cast<int64_t>(g) * kDV * kDC;
+#pragma unroll
+    for (int ft = 0; ft < 2; ++ft)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        wf[ft][ks] = *reinterpret_cast<const bf16x8*>(wmat + static_cast<int64_t>(row0 + 16 * ft + col) * kDC + 32 * ks + 8 * grp);
+    {
+      const int sw = swz(col);
+      const int lo2 = (grp ^ sw) & 3;
+      base_even = col * kRowBytes + 16 * ((0 ^ (sw & 4)) | lo2);
+      base_odd = col * kRowBytes + 16 * ((4 ^ (sw & 4)) | lo2);
+    }
+    for (int i = threadIdx.x; i < nj; i += W * 64) {
+      const int32_t id = ids[j0 + i];
+      e_ids[i] = (id < 0 || id >= num_blocks) ? -1 : id;
+    }
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    lds_barrier();
+    issue<0>(0);
+    for (int j = 0; j < nj; j += 2) {
+      step<0>(j);
+      step<1>(j + 1);
+    }
+    wait_vmcnt<0>();
+  }
+};
+
+template <int DN>
+__global__ __launch_bounds__((DN + kDV) / 32 * 64, 1) void expand_blocks(ProjParams d, const bf16_t* latent, const bf16_t* w_uk,
+                                                                         const bf16_t* w_uv, const int32_t* ids, int64_t n_ids,
+                                                                         int64_t num_blocks, int per_wg, bf16_t* expanded) {
+  const int64_t j0 = static_cast<int64_t>(blockIdx.x) * per_wg;
+  const int nj = static_cast<int>(min<int64_t>(per_wg, n_ids - j0));
+  if (nj <= 0) return;
+  ExpandCta<DN> cta(d, latent, ids, num_blocks, expanded);
+  cta.run(w_uk, w_uv, static_cast<int>(j0), nj, blockIdx.y);
+}
+
+}  // namespace
+
+bool tuned_expand_supported(const gqla_dims* d) {
+  return d->dtype == GQLA_BF16 && d->latent_rank == kDC && d->rope_dim == kDR && d->v_dim == kDV &&
+         (d->nope_dim == 64 || d->nope_dim == 128);
+}
+
+hipError_t launch_tuned_expand(const ProjParams& p, const void* latent, const void* w_uk, const void* w_uv,
+                               const int32_t* block_ids, int64_t n_blocks, int64_t num_blocks, void* expanded,
+                               hipStream_t s) {
+  // Enough workgroups to cover the CUs, each holding its group's weights for a run of blocks.
+  const int64_t per_group = std::max<int64_t>(1, (2 * kNumCUs + p.G - 1) / p.G);
+  const int per_wg = static_cast<int>(std::min<int64_t>(kMaxRun, std::max<int64_t>(1, (n_blocks + per_group - 1) / per_group)));
+  const int64_t wgs = (n_blocks + per_wg - 1) / per_wg;
+  if (wgs > 0x7fffffff) return hipErrorInvalidConfiguration;
+  dim3 grid(static_cast<unsigned>(wgs), p.G);
+  const bf16_t* lat = static_cast<const bf16_t*>(latent);
+  const bf16_t* wk = static_cast<const bf16_t*>(w_uk);
+  const bf16_t* wv = static_cast<const bf16_t*>(w_uv);
+  bf16_t* ex = static_cast<bf16_t*>(expanded);
+  if (p.dn == 128)
+    expand_blocks<128><<<grid, (128 + kDV) / 32 * 64, 0, s>>>(p, lat, wk, wv, block_ids, n_blocks, num_blocks, per_wg, ex);
+  else
+    expand_blocks<64><<<grid, (64 + kDV) / 32 * 64, 0, s>>>(p, lat, wk, wv, block_ids, n_blocks, num_blocks, per_wg, ex);
+  return hipGetLastError();
+}
+
+}  // namespace gqla
