@@ -45,8 +45,13 @@ constexpr int kTileBytes = kBlock * kRowBytes;  // 73728
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Swizzle of a token row's 16-byte chunk index inside its 128-byte group.
-__device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+// Swizzle of a token row's 16-byte chunk index inside its 128-byte group. gfx950's LDS
+// serves 256 bytes per cycle and a 1152-byte row stride alternates rows between the two
+// 128-byte halves, so conflict-free access needs, for the score reads (16 rows, one
+// chunk each), distinct (t & 1, swz) over 16 consecutive rows, and for the transposed
+// reads (8 rows, a chunk pair each), distinct swz >> 1 among same-parity rows of each
+// aligned 8: swz(t) = (t mod 8) xor bit 3 of t satisfies both and has period 16.
+__device__ __forceinline__ int swz(int t) { return (t & 7) ^ ((t >> 3) & 1); }
 __device__ __forceinline__ int chunk_off(int t, int c) {
   return t * kRowBytes + (((c & ~7) | ((c & 7) ^ swz(t))) << 4);
 }
@@ -75,6 +80,12 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+}
+
+// One 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4): lane l's bytes
+// land at lds + 16 * l.
+__device__ __forceinline__ void copy16_to_lds(const char* g, lds_void* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
 }
 
 constexpr int kMaxSplitBlocks = 2048;    // block ids of one split staged in LDS
@@ -112,6 +123,7 @@ struct AbsorbCta {
   // per-lane LDS byte offsets (see score() and value())
   int s_base_even, s_base_odd;
   int v_base[4];
+  int dma_off[PER_WAVE];   // per-lane source offsets of the tile copy
 
   __device__ AbsorbCta(const AttnParams& p_) : p(p_) {}
 
@@ -122,16 +134,26 @@ struct AbsorbCta {
   __device__ __forceinline__ void issue(int k) {
     const int32_t id = max(g_ids[k], 0);   // invalid ids already poisoned the output
     const char* src = static_cast<const char*>(p.kv) + static_cast<int64_t>(id) * kTileBytes;
-    int ln = lane;
-    asm volatile("" : "+v"(ln));           // recompute offsets here instead of holding them
 #pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) {
-      const int slot = (wave * PER_WAVE + j) * 64 + ln;
-      const int t = slot / kChunks, cp = slot - t * kChunks;
-      const int c = (cp & ~7) | ((cp & 7) ^ swz(t));
-      __builtin_amdgcn_global_load_lds(src + (t * kRowBytes + c * 16),
-                                       (lds_void*)(tile_buf<BUF>() + (wave * PER_WAVE + j) * 1024), 16, 0, 0);
-    }
+    for (int j = 0; j < PER_WAVE; ++j)
+      copy16_to_lds(src + dma_off[j], (lds_void*)(tile_buf<BUF>() + (wave * PER_WAVE + j) * 1024));
+  }
+
+  // Byte offset, inside a block, of the chunk that lands in LDS slot `slot` of a tile.
+  __device__ __forceinline__ static int slot_source(int slot) {
+    const int t = slot / kChunks, cp = slot - t * kChunks;
+    return t * kRowBytes + 16 * ((cp & ~7) | ((cp & 7) ^ swz(t)));
+  }
+
+  // Slots past the context in the last block hold arbitrary bits: zero those token rows
+  // in LDS once, so the value product needs no per-element masking.
+  template <int BUF>
+  __device__ __forceinline__ void clear_tail(int valid) {
+    char* tile = tile_buf<BUF>();
+    for (int i = valid * kChunks + threadIdx.x; i < kBlock * kChunks; i += W * 64)
+      *reinterpret_cast<uint4*>(tile + 16 * i) = uint4{0u, 0u, 0u, 0u};
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    lds_barrier();
   }
 
   // Scores S^T = C Q^T of the 32 tokens t0 .. t0+31 for each row tile of the wave.
@@ -169,7 +191,7 @@ struct AbsorbCta {
   // feeds ds_read_b64_tr_b16 with 4 features 4*(col&3) of token row col>>2. Per-lane
   // bases exist for the four values of ft & 3; the rest is a compile-time offset.
   template <int BUF>
-  __device__ __forceinline__ void value(int t0, const bf16x8 (&pf)[RPW], int tb, bool last) {
+  __device__ __forceinline__ void value(int t0, const bf16x8 (&pf)[RPW]) {
     const char* tile = tile_buf<BUF>() + t0 * kRowBytes;
     auto tr = [&](int ft, int second) {
       return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -180,13 +202,6 @@ struct AbsorbCta {
     for (int ft = 0; ft < FT; ++ft) {
       i16x4 lo2 = lo1, hi2 = hi1;
       if (ft + 2 < FT) { lo2 = tr(ft + 2, 0); hi2 = tr(ft + 2, 1); }
-      if (last) {   // slots past the context hold arbitrary bits
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (tb + e >= L) lo0[e] = 0;
-          if (tb + 16 + e >= L) hi0[e] = 0;
-        }
-      }
       const i16x8 av = __builtin_shufflevector(lo0, hi0, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
       for (int r = 0; r < RPW; ++r)
@@ -244,7 +259,7 @@ struct AbsorbCta {
     lds_barrier();
     if (k < nb) {
       const int blk = blk_lo + k;
-      const bool last = (blk + 1) * kBlock > L;
+      if ((blk + 1) * kBlock > L) clear_tail<BUF>(L - blk * kBlock);
       auto half_step = [&](int hh) {
         const int t0 = hh * 32;
         f32x4 s[RPW][2];
@@ -253,7 +268,7 @@ struct AbsorbCta {
         bf16x8 pf[RPW];
 #pragma unroll
         for (int r = 0; r < RPW; ++r) pf[r] = softmax(r, s[r], tb);
-        value<BUF>(t0, pf, tb, last);
+        value<BUF>(t0, pf);
       };
       if (TG == 2) {
         half_step(tg);
@@ -309,6 +324,8 @@ struct AbsorbCta {
       for (int ft = 0; ft < FT; ++ft) acc[r][ft] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     qk_scale = p.scale * kLog2e;
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) dma_off[j] = slot_source((wave * PER_WAVE + j) * 64 + lane);
     {
       const int sw = swz(col);
       const int lo2 = (grp ^ sw) & 3;

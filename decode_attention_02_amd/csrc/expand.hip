@@ -35,7 +35,9 @@ constexpr int kChunks = kDQ / 8;
 constexpr int kTileBytes = kBlock * kRowBytes;
 constexpr int kDV = 128;
 
-__device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+// Chunk swizzle of the latent tile in LDS (the absorb decode's layout: conflict-free
+// 16-row reads of one chunk on gfx950's 256-byte-per-cycle LDS).
+__device__ __forceinline__ int swz(int t) { return (t & 7) ^ ((t >> 3) & 1); }
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -47,6 +49,12 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+}
+
+// One 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4): lane l's bytes
+// land at lds + 16 * l.
+__device__ __forceinline__ void copy16_to_lds(const char* g, lds_void* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
 }
 
 __shared__ __attribute__((aligned(16))) char e_tile0[kTileBytes];
@@ -78,6 +86,7 @@ struct ExpandCta {
   int row0;                 // first weight row of this wave within its matrix
   bf16x8 wf[2][KS];         // the wave's weight rows, MFMA operand layout
   int base_even, base_odd;  // per-lane LDS offsets of the latent operand
+  int dma_off[PER_WAVE];    // per-lane source offsets of the tile copy
 
   __device__ ExpandCta(const ProjParams& d_, const bf16_t* lat, const int32_t* ids_, int64_t nb, bf16_t* ex)
       : d(d_), latent(lat), ids(ids_), num_blocks(nb), expanded(ex) {}
@@ -90,16 +99,9 @@ struct ExpandCta {
   __device__ __forceinline__ void issue(int j) {
     const int id = max(block_id(j), 0);   // skipped ids still copy a valid block
     const char* src = reinterpret_cast<const char*>(latent) + static_cast<int64_t>(id) * kTileBytes;
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
 #pragma unroll
-    for (int k = 0; k < PER_WAVE; ++k) {
-      const int slot = (wave * PER_WAVE + k) * 64 + ln;
-      const int t = slot / kChunks, cp = slot - t * kChunks;
-      const int c = (cp & ~7) | ((cp & 7) ^ swz(t));
-      __builtin_amdgcn_global_load_lds(src + (t * kRowBytes + c * 16),
-                                       (lds_void*)(etile<BUF>() + (wave * PER_WAVE + k) * 1024), 16, 0, 0);
-    }
+    for (int k = 0; k < PER_WAVE; ++k)
+      copy16_to_lds(src + dma_off[k], (lds_void*)(etile<BUF>() + (wave * PER_WAVE + k) * 1024));
   }
 
   // Key rows (K^T = W C^T) or value rows (V = C W^T) of one 64-token tile; the
@@ -190,6 +192,12 @@ struct ExpandCta {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         wf[ft][ks] = *reinterpret_cast<const bf16x8*>(wmat + static_cast<int64_t>(row0 + 16 * ft + col) * kDC + 32 * ks + 8 * grp);
+#pragma unroll
+    for (int k = 0; k < PER_WAVE; ++k) {
+      const int slot = (wave * PER_WAVE + k) * 64 + lane;
+      const int t = slot / kChunks, cp = slot - t * kChunks;
+      dma_off[k] = t * kRowBytes + 16 * ((cp & ~7) | ((cp & 7) ^ swz(t)));
+    }
     {
       const int sw = swz(col);
       const int lo2 = (grp ^ sw) & 3;
