@@ -10,8 +10,14 @@ dominant kernel (the GQA split-KV decode), timed with HIP events on the stream i
 on; "cpu_baseline" times the fp64 oracle on a bounded sample of the same batch.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+       python bench.py --profile            (untimed: a 1 GiB calibration copy, then steps,
+                                             for rocprofv3 counter passes)
+       python bench.py --summarize-pmc FETCH_DIR WRITE_DIR   (HBM traffic of the GQA decode
+                                             from two rocprofv3 --pmc output folders)
 """
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -24,6 +30,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+DOMINANT_SRC = os.path.join(ROOT, "decode_attention_02_amd", "csrc", "gqa_decode.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gqa_decode_split_traffic.json")
+CALIB_BYTES = 1 << 30           # plain copy used to scale FETCH_SIZE / WRITE_SIZE
 
 
 def parse():
@@ -36,7 +45,58 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--absorb-sq", type=int, default=1)
     ap.add_argument("--gqa-sq", type=int, default=2)
+    ap.add_argument("--profile", action="store_true")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     return ap.parse_args()
+
+
+def source_sha(path=DOMINANT_SRC):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def summarize_pmc(fetch_dir, write_dir, workload_name):
+    """Per-dispatch HBM traffic of the GQA decode kernel from FETCH_SIZE / WRITE_SIZE
+    passes, each scaled by what the counter reads for the 1 GiB calibration copy."""
+    def per_kernel(d, counter):
+        rows = list(csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))))
+        disp = {}
+        for r in rows:
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Kernel_Name"], int(r["Dispatch_Id"]))
+            disp[key] = disp.get(key, 0.0) + float(r["Counter_Value"]) * 1024.0   # KiB -> bytes
+        out = {}
+        for (name, _), v in disp.items():
+            out.setdefault(name, []).append(v)
+        return out
+    f, wr = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    copy = [k for k in f if "copy" in k.lower() or "elementwise" in k.lower()]
+    gqa = [k for k in f if "gqa_decode_split" in k]
+    if not copy or not gqa:
+        raise SystemExit(f"kernels not found: {list(f)}")
+    big = max(copy, key=lambda k: max(f[k]))
+    f_scale = CALIB_BYTES / max(f[big])                 # copy reads CALIB_BYTES
+    w_scale = CALIB_BYTES / max(wr.get(big, [0.0]))     # and writes CALIB_BYTES
+    fetch = float(np.mean(f[gqa[0]])) * f_scale
+    write = float(np.mean(wr[gqa[0]])) * w_scale
+    return {"workload": workload_name, "kernel": gqa[0], "source_sha256": source_sha(),
+            "fetch_bytes": fetch, "write_bytes": write, "traffic_bytes": fetch + write,
+            "raw_fetch_bytes": float(np.mean(f[gqa[0]])), "raw_write_bytes": float(np.mean(wr[gqa[0]])),
+            "calibration": {"copy_kernel": big, "bytes": CALIB_BYTES, "fetch_scale": f_scale, "write_scale": w_scale},
+            "commands": ["rocprofv3 --pmc FETCH_SIZE --output-format csv -d <FETCH_DIR> -o run -- python3 bench.py --profile",
+                         "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <WRITE_DIR> -o run -- python3 bench.py --profile",
+                         "python bench.py --summarize-pmc <FETCH_DIR> <WRITE_DIR>"]}
+
+
+def load_traffic(workload_name):
+    """Measured traffic of the current GQA decode source on this workload, else None."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != source_sha() or t.get("workload") != workload_name:
+        return None
+    return t["traffic_bytes"]
 
 
 def log(msg):
@@ -78,6 +138,9 @@ def cpu_baseline(x, q_abs_sq, gqa_sq, budget_s):
 
 def main():
     a = parse()
+    if a.summarize_pmc:
+        print(json.dumps(summarize_pmc(*a.summarize_pmc, a.workload), indent=1))
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {a.gpus} is not supported (this build has no "
               "multi-GPU path; the GQA path would shard its groups across ranks)", file=sys.stderr)
@@ -153,6 +216,17 @@ def main():
             ev[3].record()
             marks.append(ev)
 
+    if a.profile:   # untimed passes for rocprofv3 counters: calibration copy, then steps
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        del src, dst
+        for _ in range(3):
+            step(False)
+        torch.cuda.synchronize()
+        log("[bench] profile passes done")
+        return
     log(f"[bench] warmup {a.warmup} steps, splits {splits}")
     for _ in range(a.warmup):
         step(False)
@@ -203,7 +277,7 @@ def main():
         },
         "roofline": {"kernel": "gqa_decode_split (gqla_decode_gqa)", "bound": "hbm",
                      "achieved": kv_gqa / (t_gqa / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": kv_gqa / (t_gqa / 1e3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "frac": kv_gqa / (t_gqa / 1e3) / 1e9 / HBM_PEAK_GBS, "traffic": load_traffic(w.name),
                      "algorithmic_bytes_per_launch": kv_gqa, "avg_launch_ms": t_gqa},
     }
     if not a.no_cpu_baseline:
