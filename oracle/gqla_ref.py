@@ -91,10 +91,12 @@ def mla_expanded_attention(c, kr, w_uk, w_uv, q_nope, q_rope, s_q, scale):
     d_v = w_uv.shape[1]
     out = np.zeros((s_q, H, d_v))
     lse = np.zeros((s_q, H))
+    kv = {}   # K and V of a group, formed the first time one of its heads needs them
     for h in range(H):
         g = head_group(h, H, G)
-        k = np.concatenate([c @ w_uk[g].T, kr], axis=1)
-        v = c @ w_uv[g].T
+        if g not in kv:
+            kv[g] = (np.concatenate([c @ w_uk[g].T, kr], axis=1), c @ w_uv[g].T)
+        k, v = kv[g]
         for i in range(s_q):
             n = visible_tokens(L, s_q, i)
             q = np.concatenate([q_nope[i, h], q_rope[i, h]])
