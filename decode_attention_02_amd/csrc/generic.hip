@@ -140,47 +140,56 @@ hipError_t launch_generic_attn(const AttnParams& p, bool bf16, hipStream_t s) {
 }
 
 // Merge split partials: o = sum_s w_s o_s / sum_s w_s, w_s = exp(lse_s - max lse);
-// lse = max + ln sum w. A NaN partial (bad metadata) makes the row NaN.
-__global__ __launch_bounds__(256) void combine_splits(CombineParams c) {
-  __shared__ float w[1024];
-  __shared__ float tot_s, m_s;
-  __shared__ int nan_s;
+// lse = max + ln sum w. A NaN partial (bad metadata) makes the row NaN. Every thread
+// derives the weights itself from the row's lse values (L2-resident), then handles four
+// consecutive features with 16-byte loads.
+__global__ __launch_bounds__(128) void combine_splits(CombineParams c) {
   const int64_t row = blockIdx.x;
-  const int tid = threadIdx.x;
-  if (tid == 0) {
-    float m = -INFINITY;
-    int has_nan = 0;
-    for (int s = 0; s < c.n_split; ++s) {
-      const float l = c.ws_lse[row * c.n_split + s];
-      if (l != l) has_nan = 1;
-      else m = fmaxf(m, l);
-    }
-    float tot = 0.f;
-    for (int s = 0; s < c.n_split; ++s) {
-      const float l = c.ws_lse[row * c.n_split + s];
-      const float e = (has_nan || l == -INFINITY) ? 0.f : expf(l - m);
-      w[s] = e;
-      tot += e;
-    }
-    tot_s = tot;
-    m_s = m;
-    nan_s = has_nan || !(tot > 0.f);
+  const float* lse = c.ws_lse + row * c.n_split;
+  float m = -INFINITY;
+  bool has_nan = false;
+  for (int s = 0; s < c.n_split; ++s) {
+    const float l = lse[s];
+    has_nan |= l != l;
+    m = fmaxf(m, l);
   }
-  __syncthreads();
-  const float inv = 1.f / tot_s;
-  for (int f = tid; f < c.dvo; f += blockDim.x) {
-    float acc = 0.f;
-    for (int s = 0; s < c.n_split; ++s) {
-      if (w[s] != 0.f) acc += w[s] * c.ws_o[(row * c.n_split + s) * c.dvo + f];
-    }
-    store_out(c.out, c.out_kind, row * c.dvo + f, nan_s ? nan_f32() : acc * inv);
+  float tot = 0.f;
+  for (int s = 0; s < c.n_split; ++s) {
+    const float l = lse[s];
+    tot += (l == -INFINITY) ? 0.f : expf(l - m);
   }
-  if (c.lse != nullptr && tid == 0) c.lse[row] = nan_s ? nan_f32() : m_s + logf(tot_s);
+  const bool nan_row = has_nan || !(tot > 0.f);
+  const float inv = 1.f / tot;
+  const float* o = c.ws_o + row * c.n_split * c.dvo;
+  if ((c.dvo & 3) == 0) {
+    for (int f = 4 * threadIdx.x; f < c.dvo; f += 4 * blockDim.x) {
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int s = 0; s < c.n_split; ++s) {
+        const float l = lse[s];
+        if (l == -INFINITY) continue;
+        const float w = expf(l - m);
+        const float4 v = *reinterpret_cast<const float4*>(o + static_cast<int64_t>(s) * c.dvo + f);
+        acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
+      }
+      const float r[4] = {acc.x, acc.y, acc.z, acc.w};
+      for (int k = 0; k < 4; ++k) store_out(c.out, c.out_kind, row * c.dvo + f + k, nan_row ? nan_f32() : r[k] * inv);
+    }
+  } else {
+    for (int f = threadIdx.x; f < c.dvo; f += blockDim.x) {
+      float acc = 0.f;
+      for (int s = 0; s < c.n_split; ++s) {
+        const float l = lse[s];
+        if (l == -INFINITY) continue;
+        acc += expf(l - m) * o[static_cast<int64_t>(s) * c.dvo + f];
+      }
+      store_out(c.out, c.out_kind, row * c.dvo + f, nan_row ? nan_f32() : acc * inv);
+    }
+  }
+  if (c.lse != nullptr && threadIdx.x == 0) c.lse[row] = nan_row ? nan_f32() : m + logf(tot);
 }
 
 hipError_t launch_combine(const CombineParams& c, hipStream_t s) {
-  if (c.n_split > 1024) return hipErrorInvalidValue;
-  combine_splits<<<c.rows, 256, 0, s>>>(c);
+  combine_splits<<<c.rows, 128, 0, s>>>(c);
   return hipGetLastError();
 }
 

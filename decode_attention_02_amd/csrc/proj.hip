@@ -7,7 +7,8 @@
 //
 // Both are grouped GEMMs with few rows per group, bound by moving the queries, the
 // latent outputs and the weights. A workgroup takes one group and 64 of its query rows
-// (4 waves x 16), stages the group's weight matrix once in LDS and forms the transposed
+// (4 waves x 16), copies the group's weight matrix once into LDS (global_load_lds, in
+// flight together with the row operands) and forms the transposed
 // product so that each lane ends with 4 consecutive output features of one row
 // (8-byte stores):
 //   * absorb query: q_abs^T = W_UK^g^T q^T contracts over W_UK's row index, so the
@@ -40,12 +41,15 @@ __device__ __forceinline__ int64_t group_row(int rg, int g, int gs, int H) {
   return static_cast<int64_t>(rg / gs) * H + g * gs + rg % gs;
 }
 
-// Copy a [rows][512] bf16 matrix into LDS with the padded row stride.
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Copy a [rows][512] bf16 weight matrix into LDS rows of stride kPadRow: one
+// global_load_lds_dwordx4 per 1 KiB row (lane l brings bytes 16l..16l+15), so the copy
+// needs no registers and every wave's share is in flight at once. Waits for it.
 __device__ __forceinline__ void stage_rows(char* lds, const bf16_t* src, int rows) {
-  for (int i = threadIdx.x; i < rows * (kDC / 8); i += blockDim.x) {
-    const int r = i / (kDC / 8), c = i % (kDC / 8);
-    *reinterpret_cast<uint4*>(lds + r * kPadRow + c * 16) = *reinterpret_cast<const uint4*>(src + r * kDC + c * 8);
-  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, waves = blockDim.x >> 6;
+  for (int r = wave; r < rows; r += waves)
+    __builtin_amdgcn_global_load_lds(src + r * kDC + 8 * lane, (lds_void*)(lds + r * kPadRow), 16, 0, 0);
 }
 
 template <int DN>
@@ -55,8 +59,6 @@ __global__ __launch_bounds__(256) void absorb_query_kernel(ProjParams d, const b
   const int g = blockIdx.y;
   const int gs = d.H / d.G;
   const int rows_g = d.rows * gs;
-  stage_rows(w, w_uk + static_cast<int64_t>(g) * DN * kDC, DN);
-  __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int rg = blockIdx.x * kRowsPerWG + wave * 16 + col;   // this lane's row (B operand column)
@@ -67,6 +69,9 @@ __global__ __launch_bounds__(256) void absorb_query_kernel(ProjParams d, const b
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
     qf[ks] = live ? *reinterpret_cast<const bf16x8*>(q_nope + row * DN + 32 * ks + 8 * grp) : bf16x8{};
+  stage_rows(w, w_uk + static_cast<int64_t>(g) * DN * kDC, DN);
+  __builtin_amdgcn_s_waitcnt(0);   // queries and this wave's weight rows have landed
+  __syncthreads();
   const int dq = kDC + kDR;
   // A operand (W^T, 16 latent features x 32 nope values): source lane `col` of each
   // 16-lane group supplies nope row 32*ks + 8*grp + 4*half + (col >> 2), features
@@ -105,23 +110,32 @@ __global__ __launch_bounds__(256) void out_proj_kernel(ProjParams d, const float
   const int g = blockIdx.y;
   const int gs = d.H / d.G;
   const int rows_g = d.rows * gs;
-  stage_rows(w, w_uv + static_cast<int64_t>(g) * kDV * kDC, kDV);
-  __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int rg = blockIdx.x * kRowsPerWG + wave * 16 + col;
   const bool live = rg < rows_g;
   const int64_t row = live ? group_row(rg, g, gs, d.H) : 0;
+  // The lane's whole slice of its latent-output row (16 k-steps x 8 values), loaded up
+  // front together with the weight copy so both are in flight at once.
+  const float* o = o_lat + row * kDC + 8 * grp;
+  f32x4 xo[kDC / 32][2];
+#pragma unroll
+  for (int ks = 0; ks < kDC / 32; ++ks) {
+    xo[ks][0] = live ? *reinterpret_cast<const f32x4*>(o + 32 * ks) : f32x4{0.f, 0.f, 0.f, 0.f};
+    xo[ks][1] = live ? *reinterpret_cast<const f32x4*>(o + 32 * ks + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  stage_rows(w, w_uv + static_cast<int64_t>(g) * kDV * kDC, kDV);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
   f32x4 acc[kDV / 16];
 #pragma unroll
   for (int vt = 0; vt < kDV / 16; ++vt) acc[vt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const float* o = o_lat + row * kDC + 8 * grp;
 #pragma unroll 2
   for (int ks = 0; ks < kDC / 32; ++ks) {
     // B operand: 8 latent values of this lane's row, as bf16 high + low parts.
     bf16x8 hi, lo;
-    const f32x4 x0 = live ? *reinterpret_cast<const f32x4*>(o + 32 * ks) : f32x4{0.f, 0.f, 0.f, 0.f};
-    const f32x4 x1 = live ? *reinterpret_cast<const f32x4*>(o + 32 * ks + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    const f32x4 x0 = xo[ks][0];
+    const f32x4 x1 = xo[ks][1];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const float x = k < 4 ? x0[k] : x1[k - 4];
