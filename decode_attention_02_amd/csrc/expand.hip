@@ -11,9 +11,9 @@
 // once per workgroup, while the latent tiles stream through LDS (global_load_lds,
 // double-buffered, the XOR-swizzled layout of the absorb decode). Key rows come out of
 // K^T = W_UK^g C^T, whose accumulator holds 4 consecutive key features of one token
-// (8-byte stores into the token-major K); value rows come out of V = C W_UV^g^T, whose
-// accumulator holds 4 consecutive tokens of one feature (8-byte stores into the
-// feature-major V). The RoPE key is copied into every group's K.
+// (8-byte stores into a 32-feature key slab); value rows come out of V = C W_UV^g^T,
+// whose accumulator holds 4 consecutive tokens of one feature (8-byte stores into a
+// 32-token value half). The RoPE key is copied into every group's K.
 #include "device_common.h"
 #include "gqla_internal.h"
 #include "tuned.h"
@@ -136,13 +136,18 @@ struct ExpandCta {
 #pragma unroll
         for (int k = 0; k < 4; ++k) packed[k] = f32_to_bf16(acc[ft][k]);
         if (KEY) {
-          // K^T tile: lane = token tt*16 + col, key features row0 + 16*ft + 4*grp + k
+          // K^T tile: lane = token tt*16 + col, key features f = row0 + 16*ft + 4*grp + k,
+          // inside the 32-feature slab f / 32
           const int tok = tt * 16 + col;
-          *reinterpret_cast<uint2*>(chunk + tok * DQK + row0 + 16 * ft + 4 * grp) = *reinterpret_cast<uint2*>(packed);
+          const int f = row0 + 16 * ft + 4 * grp;
+          *reinterpret_cast<uint2*>(chunk + (f / kSlab) * kBlock * kSlab + tok * kSlab + f % kSlab) =
+              *reinterpret_cast<uint2*>(packed);
         } else {
-          // V tile: lane = value feature row0 + 16*ft + col, tokens tt*16 + 4*grp + k
+          // V tile: lane = value feature f = row0 + 16*ft + col, tokens tok = tt*16 + 4*grp + k,
+          // inside the 32-token half tok / 32
           const int f = row0 + 16 * ft + col;
-          *reinterpret_cast<uint2*>(chunk + kBlock * DQK + f * kBlock + tt * 16 + 4 * grp) =
+          const int tok = tt * 16 + 4 * grp;
+          *reinterpret_cast<uint2*>(chunk + kBlock * DQK + (tok / kHalf) * kDV * kHalf + f * kHalf + tok % kHalf) =
               *reinterpret_cast<uint2*>(packed);
         }
       }
@@ -159,7 +164,8 @@ struct ExpandCta {
     for (int i = threadIdx.x; i < kBlock * kDR / 8; i += W * 64) {
       const int tok = i / (kDR / 8), c = kDC / 8 + i % (kDR / 8);
       const uint4 v = *reinterpret_cast<const uint4*>(tile + tok * kRowBytes + (((c & ~7) | ((c & 7) ^ swz(tok))) << 4));
-      *reinterpret_cast<uint4*>(chunk + tok * DQK + DN + 8 * (i % (kDR / 8))) = v;
+      const int f = DN + 8 * (i % (kDR / 8));
+      *reinterpret_cast<uint4*>(chunk + (f / kSlab) * kBlock * kSlab + tok * kSlab + f % kSlab) = v;
     }
   }
 

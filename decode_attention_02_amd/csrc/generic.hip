@@ -18,6 +18,21 @@ size_t generic_attn_lds_bytes(int dk, int dvo) {
   return sizeof(float) * (static_cast<size_t>(kGenRows) * (dk + kBlock + dvo) + 3 * kGenRows);
 }
 
+// Offset of key feature f of slot t inside a kv head's block: plain strides for the
+// latent, or the expanded cache's slabs (features [32s, 32s + w_s) of all 64 slots stored
+// slot-major, w_s = min(32, dk - 32s)).
+__device__ __forceinline__ int64_t kv_k_index(const AttnParams& p, int t, int f) {
+  if (p.k_slab == 0) return static_cast<int64_t>(t) * p.k_ts + static_cast<int64_t>(f) * p.k_fs;
+  const int s = f / p.k_slab;
+  const int w = min(p.k_slab, p.dk - s * p.k_slab);
+  return static_cast<int64_t>(s) * kBlock * p.k_slab + t * w + (f - s * p.k_slab);
+}
+
+__device__ __forceinline__ int64_t kv_v_index(const AttnParams& p, int t, int f) {
+  return p.v_off + static_cast<int64_t>(t / kHalf) * p.v_half + static_cast<int64_t>(t % kHalf) * p.v_ts +
+         static_cast<int64_t>(f) * p.v_fs;
+}
+
 // One workgroup = (split, row tile, sequence x kv head). Online softmax over the
 // 64-token blocks of its split: scores to LDS, row statistics, rescaled accumulation.
 template <typename T>
@@ -69,7 +84,7 @@ __global__ __launch_bounds__(kGenThreads) void generic_attn_split(AttnParams p) 
       if (blk * kBlock + t < n) {
         float acc = 0.f;
         for (int f = 0; f < p.dk; ++f)
-          acc += sq[r * p.dk + f] * Elt<T>::load(base, static_cast<int64_t>(t) * p.k_ts + static_cast<int64_t>(f) * p.k_fs);
+          acc += sq[r * p.dk + f] * Elt<T>::load(base, kv_k_index(p, t, f));
         s = acc * p.scale;
       }
       ss[idx] = s;
@@ -100,8 +115,7 @@ __global__ __launch_bounds__(kGenThreads) void generic_attn_split(AttnParams p) 
       const int lim = min(kBlock, n - blk * kBlock);   // tokens this row sees in the block
       float acc = so[idx] * sa[r];
       for (int t = 0; t < lim; ++t)
-        acc += ss[r * kBlock + t] *
-               Elt<T>::load(base, p.v_off + static_cast<int64_t>(t) * p.v_ts + static_cast<int64_t>(f) * p.v_fs);
+        acc += ss[r * kBlock + t] * Elt<T>::load(base, kv_v_index(p, t, f));
       so[idx] = acc;
     }
     __syncthreads();
@@ -252,7 +266,9 @@ hipError_t launch_generic_out_proj(const ProjParams& d, const float* o_lat, cons
   return hipGetLastError();
 }
 
-// Expanded chunk of (block id, group g): K [64][d_qk] token-major, then V [d_v][64].
+// Expanded chunk of (block id, group g): K in slabs of 32 features ([64][w_s] each, the
+// last one narrower when d_qk is not a multiple of 32), then V as two 32-slot halves
+// [d_v][32].
 template <typename T>
 __global__ __launch_bounds__(256) void generic_expand(ProjParams d, const T* latent, const T* w_uk, const T* w_uv,
                                                       const int32_t* block_ids, int64_t num_blocks, T* expanded) {
@@ -272,14 +288,15 @@ __global__ __launch_bounds__(256) void generic_expand(ProjParams d, const T* lat
     } else {
       acc = Elt<T>::load(src, static_cast<int64_t>(r) * dq + d.dc + (e - d.dn));
     }
-    Elt<T>::store(dst, idx, acc);
+    const int s = e / kSlab, w = min(kSlab, dqk - s * kSlab);
+    Elt<T>::store(dst, static_cast<int64_t>(s) * kBlock * kSlab + r * w + (e - s * kSlab), acc);
   }
   for (int idx = threadIdx.x; idx < d.dv * kBlock; idx += blockDim.x) {
     const int f = idx / kBlock, r = idx % kBlock;
     float acc = 0.f;
     for (int c = 0; c < d.dc; ++c)
       acc += Elt<T>::load(src, static_cast<int64_t>(r) * dq + c) * Elt<T>::load(w_uv, (static_cast<int64_t>(g) * d.dv + f) * d.dc + c);
-    Elt<T>::store(dst, static_cast<int64_t>(kBlock) * dqk + idx, acc);
+    Elt<T>::store(dst, static_cast<int64_t>(kBlock) * dqk + (r / kHalf) * d.dv * kHalf + f * kHalf + r % kHalf, acc);
   }
 }
 

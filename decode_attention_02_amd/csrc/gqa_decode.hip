@@ -17,8 +17,8 @@
 //     one query row: its running max/sum need only two cross-lane shuffles per step;
 //   * K rows are gathered in a permuted token order so that each lane ends up holding
 //     8 consecutive tokens, which is exactly the B-operand slice of P^T for the value
-//     product O^T = V^T P^T; V is stored feature-major, so its A operand is again one
-//     128-bit load per lane and P never leaves registers.
+//     product O^T = V^T P^T; V is stored feature-major (per 32-token half), so its A
+//     operand is again one 128-bit load per lane and P never leaves registers.
 // Rows: query row j < gs * s_q of a group is (i = j / gs, head = g * gs + j % gs);
 // rows beyond gs * s_q (up to the 16 of an MFMA tile) carry zero queries.
 #include "device_common.h"
@@ -32,14 +32,20 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Plain (temporal) loads on purpose: each K row is fetched as two 64-byte halves by
-// consecutive instructions, and the second half must find the line in L2.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ bf16x8 load8(const bf16_t* p) {
   return *reinterpret_cast<const bf16x8*>(p);
+}
+// Cache operands are read exactly once, each load covering whole 128-byte lines (the
+// expanded cache's slab layout), so they bypass cache retention.
+__device__ __forceinline__ bf16x8 load8_stream(const bf16_t* p) {
+  return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(p)));
 }
 
 __device__ __forceinline__ float xor_max(float v) {
@@ -62,7 +68,7 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_split(AttnParams p) {
   __shared__ int s_bad[kWaves];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15;          // query row owned by this lane (MFMA column)
   const int grp = lane >> 4;          // k-group of the MFMA operands
   const int split = blockIdx.x % p.n_split;
@@ -105,39 +111,68 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_split(AttnParams p) {
   const int32_t* table = p.block_table + static_cast<int64_t>(b) * p.max_blocks;
   const int blk_lo = split * p.blocks_per_split;
   const int blk_hi = bad ? blk_lo : min(nblk, blk_lo + p.blocks_per_split);
+  // This wave's blocks: first, first + kWaves, ... (n_my of them).
+  const int first = blk_lo + wave;
+  const int n_my = blk_hi > first ? (blk_hi - first + kWaves - 1) / kWaves : 0;
 
-  for (int blk = blk_lo + wave; blk < blk_hi; blk += kWaves) {
-    const int32_t id = table[blk];
-    if (id < 0 || id >= p.num_blocks) { bad = true; break; }
-    const bf16_t* chunk = kv + (static_cast<int64_t>(id) * p.kv_heads + g) * CHUNK;
+  // Block ids, 64 at a time: lane i holds the id of this wave's block 64*c + i. An id
+  // outside the pool marks the whole row bad and is replaced by 0 so loads stay in bounds.
+  int ids = 0, ids_chunk = -1;
+  auto block_id = [&](int j) -> int {
+    const int c = j >> 6;
+    if (c != ids_chunk) {
+      const int jj = 64 * c + lane;
+      const int v = jj < n_my ? table[first + kWaves * jj] : 0;
+      const bool inval = jj < n_my && (v < 0 || v >= p.num_blocks);
+      bad |= __ballot(inval) != 0;
+      ids = inval ? 0 : v;
+      ids_chunk = c;
+    }
+    return __builtin_amdgcn_readlane(ids, j & 63);
+  };
+  auto chunk_of = [&](int id) -> const bf16_t* {
+    return kv + (static_cast<int64_t>(id) * p.kv_heads + g) * CHUNK;
+  };
+
+  // One block's operands: K rows of both 32-token halves, permuted so lane group `grp`
+  // gets tokens 32*half + 8*grp .. +8, and V^T slices of the same tokens. K features
+  // 32*ks .. +32 of all 64 tokens form one slab ([64][32]), V^T is stored as two 32-token
+  // halves ([DV][32]): each load instruction reads four 256-byte runs of K or one 1 KiB
+  // run of V^T.
+  struct Frag {
+    bf16x8 k[2][2][KS];
+    bf16x8 v[2][NT];
+  };
+  auto load = [&](Frag& f, const bf16_t* chunk) {
     const bf16_t* vt = chunk + kBlock * DQK;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const int t0 = half * 32;
-      // K rows for the two 16-token tiles, permuted so lane group `grp` gets tokens
-      // t0 + 8*grp .. +8 of this half.
-      bf16x8 kf[2][KS];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const int tok = t0 + 8 * (col >> 2) + 4 * tt + (col & 3);
-        const bf16_t* krow = chunk + tok * DQK + 8 * grp;
+        const int tok = 32 * half + 8 * (col >> 2) + 4 * tt + (col & 3);
+        const bf16_t* krow = chunk + tok * kSlab + 8 * grp;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kf[tt][ks] = load8(krow + 32 * ks);
+        for (int ks = 0; ks < KS; ++ks) f.k[half][tt][ks] = load8_stream(krow + ks * kBlock * kSlab);
       }
-      bf16x8 vf[NT];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) vf[nt] = load8(vt + (16 * nt + col) * kBlock + t0 + 8 * grp);
+      for (int nt = 0; nt < NT; ++nt)
+        f.v[half][nt] = load8_stream(vt + half * DV * kHalf + (16 * nt + col) * kHalf + 8 * grp);
+    }
+  };
 
+  auto compute = [&](const Frag& f, int blk) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
       f32x4 s[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[tt][ks], qf[ks], s[tt], 0, 0, 0);
+          s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.k[half][tt][ks], qf[ks], s[tt], 0, 0, 0);
       }
-      // Token of score s[tt][k] in this lane: blk*64 + t0 + 8*grp + 4*tt + k.
-      const int tbase = blk * kBlock + t0 + 8 * grp;
+      // Token of score s[tt][k] in this lane: blk*64 + 32*half + 8*grp + 4*tt + k.
+      const int tbase = blk * kBlock + 32 * half + 8 * grp;
       float sc[8];
       float mx = -INFINITY;
 #pragma unroll
@@ -162,19 +197,36 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_split(AttnParams p) {
         pf[k] = static_cast<__bf16>(e);
       }
       l_run = l_run * alpha + psum;
-      // Slots past the context hold arbitrary bits: zero those value columns.
-      if (blk * kBlock + t0 + 32 > L) {
+      // Slots past the context hold arbitrary bits (possibly NaN): their value columns
+      // are masked to zero, two tokens per 32-bit word.
+      u32x4 keep = {~0u, ~0u, ~0u, ~0u};
+      if (blk * kBlock + kBlock > L) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int k = 0; k < 8; ++k)
-            if (tbase + k >= L) vf[nt][k] = static_cast<__bf16>(0.f);
+        for (int w = 0; w < 4; ++w)
+          keep[w] = (tbase + 2 * w < L ? 0xffffu : 0u) | (tbase + 2 * w + 1 < L ? 0xffff0000u : 0u);
       }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
+        const bf16x8 vm = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, f.v[half][nt]) & keep);
         acc[nt] *= alpha;
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[nt], pf, acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vm, pf, acc[nt], 0, 0, 0);
       }
+    }
+  };
+
+  // Two blocks in flight per wave: the next block's loads are issued before the current
+  // one is consumed. Past the last block the last one is fetched again (an L2 hit), so
+  // every iteration issues the same loads and the waits stay exact.
+  if (n_my > 0) {
+    Frag fa, fb;
+    load(fa, chunk_of(block_id(0)));
+    for (int j = 0; j < n_my; j += 2) {
+      load(fb, chunk_of(block_id(min(j + 1, n_my - 1))));
+      __builtin_amdgcn_sched_barrier(0);
+      compute(fa, first + kWaves * j);
+      load(fa, chunk_of(block_id(min(j + 2, n_my - 1))));
+      __builtin_amdgcn_sched_barrier(0);
+      if (j + 1 < n_my) compute(fb, first + kWaves * (j + 1));
     }
   }
 

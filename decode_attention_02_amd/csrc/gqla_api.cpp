@@ -147,11 +147,13 @@ gqla_status run_decode(const gqla_dims* d, const gqla_paged* pg, int32_t path, c
     a.dvo = d->v_dim;
     a.kvh_stride = static_cast<int64_t>(gqla::kBlock) * (dqk + d->v_dim);
     a.block_stride = a.kvh_stride * d->num_groups;
-    a.k_ts = dqk;
-    a.k_fs = 1;
+    a.k_ts = 0;
+    a.k_fs = 0;
+    a.k_slab = gqla::kSlab;
     a.v_off = gqla::kBlock * dqk;
+    a.v_half = gqla::kHalf * d->v_dim;
     a.v_ts = 1;
-    a.v_fs = gqla::kBlock;
+    a.v_fs = gqla::kHalf;
   } else {
     const int dq = d->latent_rank + d->rope_dim;
     a.kv_heads = 1;
@@ -162,7 +164,9 @@ gqla_status run_decode(const gqla_dims* d, const gqla_paged* pg, int32_t path, c
     a.block_stride = static_cast<int64_t>(gqla::kBlock) * dq;
     a.k_ts = dq;
     a.k_fs = 1;
+    a.k_slab = 0;
     a.v_off = 0;
+    a.v_half = gqla::kHalf * dq;
     a.v_ts = dq;
     a.v_fs = 1;
   }

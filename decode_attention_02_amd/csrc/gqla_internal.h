@@ -7,6 +7,8 @@
 namespace gqla {
 
 constexpr int kBlock = 64;        // tokens per cache block
+constexpr int kSlab = 32;         // key features per slab of the expanded cache
+constexpr int kHalf = 32;         // tokens per value half-slab of the expanded cache
 constexpr int kNumCUs = 256;      // MI355X compute units (split-KV planning)
 
 enum OutKind : int32_t { OUT_F32 = 0, OUT_BF16 = 1 };
@@ -26,8 +28,9 @@ struct AttnParams {
   int32_t B, H, s_q;
   int32_t kv_heads, heads_per_kv;
   int32_t dk, dvo;               // key width, value/output width
-  int32_t k_ts, k_fs;            // K(t, f) at k_ts * t + k_fs * f
-  int32_t v_off, v_ts, v_fs;     // V(t, f) at v_off + v_ts * t + v_fs * f
+  int32_t k_ts, k_fs;            // K(t, f) at k_ts * t + k_fs * f (k_slab == 0)
+  int32_t k_slab;                // > 0: K in feature slabs of this width (see kv_k_index)
+  int32_t v_off, v_half, v_ts, v_fs;   // V(t, f) at v_off + v_half*(t/32) + v_ts*(t%32) + v_fs*f
   float scale;
   int32_t n_split, blocks_per_split;
   float* ws_o;                   // [B*s_q*H][n_split][dvo]   (n_split > 1)

@@ -146,8 +146,13 @@ gqla_status gqla_out_proj(const gqla_dims* dims, const float* o_lat, const void*
  *   block_ids      : device int32 [n_blocks], physical blocks to (re)expand; ids outside
  *                    [0, num_blocks) are skipped
  *   expanded_cache : data [num_blocks][G][64*d_qk + d_v*64]; per (block, group) chunk:
- *                    K token-major [64][d_qk] (k_nope | k_rope), then V feature-major
- *                    [d_v][64] (value feature f of slot r at f*64 + r)
+ *                    K = [k_nope | k_rope] in slabs of 32 features: slab s holds
+ *                    features [32s, 32s + w_s), w_s = min(32, d_qk - 32s), for all 64
+ *                    slots, slot-major (feature f of slot r at 2048*(f/32) + r*w_s + f%32);
+ *                    then V in two halves of 32 slots, each feature-major [d_v][32]
+ *                    (feature f of slot r at 64*d_qk + 32*d_v*(r/32) + 32*f + r%32).
+ *                    (With these slabs each wide load of the decode kernel covers
+ *                    whole 128-byte lines of a bf16 cache.)
  */
 gqla_status gqla_expand_cache(const gqla_dims* dims, const void* latent_cache, const void* w_uk,
                               const void* w_uv, const int32_t* block_ids, int64_t n_blocks,

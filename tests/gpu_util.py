@@ -95,20 +95,35 @@ class Run:
         return dict(out=to_host(out), lse=to_host(lse), expanded=expanded)
 
 
+def _slab_widths(dqk: int):
+    return [min(32, dqk - s) for s in range(0, dqk, 32)]
+
+
 def expanded_to_logical(flat: np.ndarray, num_blocks: int, G: int, dqk: int, dv: int):
     """Read the documented expanded-cache layout back into K [NB][G][64][dqk] and
-    V [NB][G][64][dv] (token-major) for comparison."""
+    V [NB][G][64][dv] (token-major) for comparison. Per (block, group) chunk: K as
+    slabs of 32 features, each [64 slots][width]; then V as two 32-slot halves, each
+    [dv][32]."""
     chunk = flat.reshape(num_blocks, G, 64 * (dqk + dv))
-    K = chunk[:, :, :64 * dqk].reshape(num_blocks, G, 64, dqk)
-    V = chunk[:, :, 64 * dqk:].reshape(num_blocks, G, dv, 64).transpose(0, 1, 3, 2)
+    parts, off = [], 0
+    for w in _slab_widths(dqk):
+        parts.append(chunk[:, :, off:off + 64 * w].reshape(num_blocks, G, 64, w))
+        off += 64 * w
+    K = np.concatenate(parts, axis=3)
+    V = chunk[:, :, off:].reshape(num_blocks, G, 2, dv, 32).transpose(0, 1, 2, 4, 3).reshape(num_blocks, G, 64, dv)
     return K, V
 
 
 def logical_to_expanded(K: np.ndarray, V: np.ndarray) -> np.ndarray:
     """Inverse of expanded_to_logical."""
-    NB, G = K.shape[:2]
-    Vt = V.transpose(0, 1, 3, 2).reshape(NB, G, -1)
-    return np.concatenate([K.reshape(NB, G, -1), Vt], axis=2).reshape(-1)
+    NB, G, _, dqk = K.shape
+    dv = V.shape[3]
+    parts, s = [], 0
+    for w in _slab_widths(dqk):
+        parts.append(K[:, :, :, s:s + w].reshape(NB, G, -1))
+        s += w
+    parts.append(V.reshape(NB, G, 2, 32, dv).transpose(0, 1, 2, 4, 3).reshape(NB, G, -1))
+    return np.concatenate(parts, axis=2).reshape(-1)
 
 
 def oracle_paths(x, seqs=None):
