@@ -85,11 +85,13 @@ __device__ __forceinline__ void lds_barrier() {
 // One 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4): lane l's bytes
 // land at lds + 16 * l.
 __device__ __forceinline__ void copy16_to_lds(const char* g, lds_void* lds) {
-  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 2);
 }
 
 constexpr int kMaxSplitBlocks = 2048;    // block ids of one split staged in LDS
 constexpr float kRescaleSlack = 8.f;     // log2 headroom before the accumulator is rescaled
+constexpr int kScoreBatch = 6;           // score operand reads per batch (36 per 32 tokens)
+constexpr int kValueBatch = 4;           // value feature tiles per batch (2 reads each)
 
 // The two tile buffers are distinct LDS objects so that the compiler can see that a
 // copy into one never aliases reads of the other, and keeps the copy in flight.
@@ -108,6 +110,9 @@ struct AbsorbCta {
   static constexpr int W = WR * TG;
   static constexpr int PER_WAVE = kChunks * kBlock / 64 / W;   // 1 KiB copies per wave per tile
   static_assert(PER_WAVE * W * 64 == kChunks * kBlock, "tile must split evenly over waves");
+  // Each wave copies whole 16-row periods of the swizzle, so its copy pattern is the same
+  // lane pattern at a wave-uniform (scalar) offset.
+  static_assert((PER_WAVE * 64) % (16 * kChunks) == 0, "wave copy block must hold whole swizzle periods");
   static constexpr int FT = kDC / 16;                          // feature tiles of O^T
   static constexpr int KS = kDQ / 32;                          // k-steps of the score product
 
@@ -123,20 +128,27 @@ struct AbsorbCta {
   // per-lane LDS byte offsets (see score() and value())
   int s_base_even, s_base_odd;
   int v_base[4];
-  int dma_off[PER_WAVE];   // per-lane source offsets of the tile copy
+  uint32_t dma_off[PER_WAVE];   // per-lane source offsets of the tile copy, within the wave's rows
 
   __device__ AbsorbCta(const AttnParams& p_) : p(p_) {}
 
-  // Copy the tile of the k-th block of the split into buffer BUF. Wave instruction j
+  // Copy of the tile of the k-th block of the split into buffer BUF. Wave instruction j
   // writes LDS slots (wave * PER_WAVE + j) * 64 + lane, each a 16-byte chunk; the lane
   // fetches the logical chunk that the swizzle stores at its slot.
-  template <int BUF>
-  __device__ __forceinline__ void issue(int k) {
+  __device__ __forceinline__ const char* tile_src(int k) const {
     const int32_t id = max(g_ids[k], 0);   // invalid ids already poisoned the output
-    const char* src = static_cast<const char*>(p.kv) + static_cast<int64_t>(id) * kTileBytes;
-#pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j)
-      copy16_to_lds(src + dma_off[j], (lds_void*)(tile_buf<BUF>() + (wave * PER_WAVE + j) * 1024));
+    return static_cast<const char*>(p.kv) + static_cast<int64_t>(id) * kTileBytes + wave * PER_WAVE * 1024;
+  }
+  template <int BUF, int J>
+  __device__ __forceinline__ void issue_one(const char* src) {
+    copy16_to_lds(src + dma_off[J], (lds_void*)(tile_buf<BUF>() + (wave * PER_WAVE + J) * 1024));
+  }
+  template <int BUF, int J = 0>
+  __device__ __forceinline__ void issue_all(const char* src) {
+    if constexpr (J < PER_WAVE) {
+      issue_one<BUF, J>(src);
+      issue_all<BUF, J + 1>(src);
+    }
   }
 
   // Byte offset, inside a block, of the chunk that lands in LDS slot `slot` of a tile.
@@ -160,54 +172,82 @@ struct AbsorbCta {
   // Chunk 4*ks + grp of token row `tok` sits at tok*1152 + 16*(...) per the swizzle;
   // since tok = t0 + 16*tt + col with t0 + 16*tt a multiple of 8, swz(tok) = swz(col)
   // and the address is a per-lane base (even or odd ks) plus a compile-time offset.
-  template <int BUF>
-  __device__ __forceinline__ void score(int t0, f32x4 (&s)[RPW][2]) {
+  // The two 16-token tiles are independent MFMA chains, interleaved. Operand reads go
+  // in batches: batch k + 1 is issued right after the first MFMA of batch k, so the
+  // single wait per batch (the compiler drains the LDS counter completely while tile
+  // copies into LDS are in flight) finds its data already landed.
+  // Copies J0 .. J0+CNT-1 of the next tile (into the other buffer, when `nxt` is set) ride
+  // along, one after every (2 * KS) / CNT MFMAs, so the copy stream never stalls the wave
+  // for long and keeps running while it computes.
+  template <int BUF, int J0, int CNT>
+  __device__ __forceinline__ void score(int t0, f32x4 (&s)[RPW][2], const char* nxt) {
     const char* tile = tile_buf<BUF>() + t0 * kRowBytes;
+    constexpr int N = 2 * KS;   // operand i = (ks = i / 2, tt = i % 2)
+    constexpr int D = kScoreBatch;
+    static_assert(N % D == 0, "score batches");
+    auto ld = [&](int i) {
+      const int ks = i >> 1, tt = i & 1;
+      return *reinterpret_cast<const bf16x8*>(tile + tt * 16 * kRowBytes + ((ks & 1) ? s_base_odd : s_base_even) +
+                                              128 * (ks >> 1));
+    };
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int r = 0; r < RPW; ++r) s[r][0] = s[r][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 a[N];
 #pragma unroll
-      for (int r = 0; r < RPW; ++r) s[r][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      auto ld = [&](int ks) {
-        return *reinterpret_cast<const bf16x8*>(tile + tt * 16 * kRowBytes + ((ks & 1) ? s_base_odd : s_base_even) +
-                                                128 * (ks >> 1));
-      };
-      bf16x8 a0 = ld(0), a1 = ld(1);
+    for (int i = 0; i < D; ++i) a[i] = ld(i);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        bf16x8 a2 = a1;
-        if (ks + 2 < KS) a2 = ld(ks + 2);
+    for (int i = 0; i < N; ++i) {
 #pragma unroll
-        for (int r = 0; r < RPW; ++r)
-          s[r][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[r][ks], s[r][tt], 0, 0, 0);
-        a0 = a1;
-        a1 = a2;
-        __builtin_amdgcn_sched_barrier(0);
+      for (int r = 0; r < RPW; ++r)
+        s[r][i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], qf[r][i >> 1], s[r][i & 1], 0, 0, 0);
+      if (i % D == 0 && i + D < N) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) a[i + D + j] = ld(i + D + j);
       }
+      constexpr int GAP = N / CNT;
+      if constexpr (CNT > 0) {
+        if (i % GAP == GAP - 1 && i / GAP < CNT && nxt != nullptr) copy_at<1 - BUF, J0>(i / GAP, nxt);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // Copy J0 + j (j runtime but in [0, CNT), resolved by a compile-time switch).
+  template <int BUF, int J0, int J = J0>
+  __device__ __forceinline__ void copy_at(int j, const char* src) {
+    if constexpr (J < PER_WAVE) {
+      if (j == J - J0) issue_one<BUF, J>(src);
+      else copy_at<BUF, J0, J + 1>(j, src);
     }
   }
 
   // O^T += C^T P^T over the 32 tokens t0 .. t0+31: lane (feature f, group grp) needs the
   // latent of tokens t0 + 4*grp + {0..3} and t0 + 16 + 4*grp + {0..3}; each 16-lane group
   // feeds ds_read_b64_tr_b16 with 4 features 4*(col&3) of token row col>>2. Per-lane
-  // bases exist for the four values of ft & 3; the rest is a compile-time offset.
+  // bases exist for the four values of ft & 3; the rest is a compile-time offset. The
+  // transposed reads are batched like the score operands.
   template <int BUF>
   __device__ __forceinline__ void value(int t0, const bf16x8 (&pf)[RPW]) {
     const char* tile = tile_buf<BUF>() + t0 * kRowBytes;
+    constexpr int D = kValueBatch;
+    static_assert(FT % D == 0, "value batches");
     auto tr = [&](int ft, int second) {
       return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_i16x4*)(tile + v_base[ft & 3] + 128 * (ft >> 2) + second * 16 * kRowBytes));
     };
-    i16x4 lo0 = tr(0, 0), hi0 = tr(0, 1), lo1 = tr(1, 0), hi1 = tr(1, 1);
+    i16x4 lo[FT], hi[FT];
+#pragma unroll
+    for (int ft = 0; ft < D; ++ft) { lo[ft] = tr(ft, 0); hi[ft] = tr(ft, 1); }
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) {
-      i16x4 lo2 = lo1, hi2 = hi1;
-      if (ft + 2 < FT) { lo2 = tr(ft + 2, 0); hi2 = tr(ft + 2, 1); }
-      const i16x8 av = __builtin_shufflevector(lo0, hi0, 0, 1, 2, 3, 4, 5, 6, 7);
+      const i16x8 av = __builtin_shufflevector(lo[ft], hi[ft], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
       for (int r = 0; r < RPW; ++r)
         acc[r][ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), pf[r], acc[r][ft], 0, 0, 0);
-      lo0 = lo1; hi0 = hi1;
-      lo1 = lo2; hi1 = hi2;
+      if (ft % D == 0 && ft + D < FT) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) { lo[ft + D + j] = tr(ft + D + j, 0); hi[ft + D + j] = tr(ft + D + j, 1); }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -246,44 +286,45 @@ struct AbsorbCta {
     return pf;
   }
 
-  // One 64-token block held in buffer BUF (k-th block of the split), with the copy of
-  // block k + 1 into the other buffer issued first.
-  // One 64-token block slot held in buffer BUF: first issue the copy of the next block
-  // (clamped to the last one, a re-read that hits L2) into the other buffer, so every
-  // step issues the same copies and the compiler can track which buffer each LDS read
-  // depends on; slots past the split's last block only keep that rhythm.
+  // One 64-token block slot held in buffer BUF (k-th block of the split): wait for its
+  // copy, then compute it while the copy of block k + 1 into the other buffer is issued
+  // piecemeal from inside the score loop. The other buffer is free: every wave passed the
+  // closing barrier of the previous step.
   template <int BUF>
   __device__ __forceinline__ void step(int k) {
-    issue<1 - BUF>(min(k + 1, nb - 1));
-    wait_vmcnt<PER_WAVE>();
+    wait_vmcnt<0>();
     lds_barrier();
     if (k < nb) {
       const int blk = blk_lo + k;
+      const char* nxt = k + 1 < nb ? tile_src(k + 1) : nullptr;
       if ((blk + 1) * kBlock > L) clear_tail<BUF>(L - blk * kBlock);
-      auto half_step = [&](int hh) {
-        const int t0 = hh * 32;
-        f32x4 s[RPW][2];
-        score<BUF>(t0, s);
-        const int tb = blk * kBlock + t0 + 4 * grp;
-        bf16x8 pf[RPW];
-#pragma unroll
-        for (int r = 0; r < RPW; ++r) pf[r] = softmax(r, s[r], tb);
-        value<BUF>(t0, pf);
-      };
-      if (TG == 2) {
-        half_step(tg);
+      if constexpr (TG == 2) {
+        half_step<BUF, 0, PER_WAVE>(tg, blk, nxt);
       } else {
-        half_step(0);
-        half_step(1);
+        static_assert(PER_WAVE % 2 == 0, "copies split over the two halves");
+        half_step<BUF, 0, PER_WAVE / 2>(0, blk, nxt);
+        half_step<BUF, PER_WAVE / 2, PER_WAVE / 2>(1, blk, nxt);
       }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     lds_barrier();
   }
 
+  template <int BUF, int J0, int CNT>
+  __device__ __forceinline__ void half_step(int hh, int blk, const char* nxt) {
+    const int t0 = hh * 32;
+    f32x4 s[RPW][2];
+    score<BUF, J0, CNT>(t0, s, nxt);
+    const int tb = blk * kBlock + t0 + 4 * grp;
+    bf16x8 pf[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) pf[r] = softmax(r, s[r], tb);
+    value<BUF>(t0, pf);
+  }
+
   __device__ __forceinline__ void run(int unit, int part) {
     lane = threadIdx.x & 63;
-    wave = threadIdx.x >> 6;
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     wr = wave % WR;
     tg = wave / WR;
     col = lane & 15;
@@ -325,7 +366,7 @@ struct AbsorbCta {
     }
     qk_scale = p.scale * kLog2e;
 #pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) dma_off[j] = slot_source((wave * PER_WAVE + j) * 64 + lane);
+    for (int j = 0; j < PER_WAVE; ++j) dma_off[j] = slot_source(j * 64 + lane);
     {
       const int sw = swz(col);
       const int lo2 = (grp ^ sw) & 3;
@@ -346,7 +387,7 @@ struct AbsorbCta {
     nb = nb_run;
     // Blocks alternate buffers 0 and 1 in pairs.
     if (nb > 0) {
-      issue<0>(0);
+      issue_all<0>(tile_src(0));
       for (int k = 0; k < nb; k += 2) {
         step<0>(k);
         step<1>(k + 1);
