@@ -20,7 +20,10 @@
 //   * small row counts (16 or 32 rows) also split each tile's two 32-token halves
 //     over two waves, merged at the end, so a workgroup still has 4 waves streaming;
 //   * more than 128 rows use two workgroups per (sequence, split), placed on the same
-//     XCD so the second tile read is served from that XCD's L2.
+//     XCD so the second tile read is served from that XCD's L2;
+//   * from 64 rows on, waves work in feature-split pairs (AbsorbPairCta): each wave
+//     scores its own 16 rows, the pair swaps P through LDS, and each wave's transposed
+//     value reads then serve both tiles for half of the latent features.
 #include "device_common.h"
 #include "gqla_internal.h"
 #include "tuned.h"
@@ -88,7 +91,7 @@ __device__ __forceinline__ void copy16_to_lds(const char* g, lds_void* lds) {
   __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 2);
 }
 
-constexpr int kMaxSplitBlocks = 2048;    // block ids of one split staged in LDS
+constexpr int kMaxSplitBlocks = 1024;    // block ids of one split staged in LDS
 constexpr float kRescaleSlack = 8.f;     // log2 headroom before the accumulator is rescaled
 constexpr int kScoreBatch = 6;           // score operand reads per batch (36 per 32 tokens)
 constexpr int kValueBatch = 4;           // value feature tiles per batch (2 reads each)
@@ -101,6 +104,12 @@ __shared__ int32_t g_ids[kMaxSplitBlocks];
 
 template <int BUF>
 __device__ __forceinline__ char* tile_buf() { return BUF == 0 ? g_tile0 : g_tile1; }
+
+// Byte offset, inside a block, of the chunk that lands in LDS slot `slot` of a tile.
+__device__ __forceinline__ int slot_source(int slot) {
+  const int t = slot / kChunks, cp = slot - t * kChunks;
+  return t * kRowBytes + 16 * ((cp & ~7) | ((cp & 7) ^ swz(t)));
+}
 
 // RPW = 16-row tiles per wave (1 or 2; two tiles share every LDS operand read),
 // RT = row tiles per workgroup, TG = waves splitting each tile's two 32-token halves.
@@ -151,11 +160,6 @@ struct AbsorbCta {
     }
   }
 
-  // Byte offset, inside a block, of the chunk that lands in LDS slot `slot` of a tile.
-  __device__ __forceinline__ static int slot_source(int slot) {
-    const int t = slot / kChunks, cp = slot - t * kChunks;
-    return t * kRowBytes + 16 * ((cp & ~7) | ((cp & 7) ^ swz(t)));
-  }
 
   // Slots past the context in the last block hold arbitrary bits: zero those token rows
   // in LDS once, so the value product needs no per-element masking.
@@ -458,6 +462,339 @@ struct AbsorbCta {
   }
 };
 
+// P operands and rescale factors that the two waves of a feature-split pair swap each
+// step: per wave, 2 halves x 64 lanes x 16 bytes, then 16 floats.
+constexpr int kXchgWave = 2 * 1024 + 64;
+__shared__ __attribute__((aligned(16))) char g_xchg[4 * kXchgWave];
+
+// Feature-split variant: waves come in pairs over two 16-row tiles. Each wave scores its
+// own tile (as above), the pair swaps the resulting P^T operands through LDS, and then
+// each wave applies the value operands it reads to BOTH tiles for one half of the 512
+// latent features. Every transposed LDS read (the most expensive LDS access here) thus
+// feeds two MFMAs, halving that traffic, while the accumulator stays 2 x 256 x 16 rows.
+// RT = row tiles per workgroup (2 or 4), TG = waves splitting each tile's 32-token halves.
+template <int RT, int TG>
+struct AbsorbPairCta {
+  static constexpr int PR = RT / 2;                            // pairs
+  static constexpr int W = RT * TG;                            // waves
+  static constexpr int NH = 2 / TG;                            // 32-token halves per wave per tile
+  static constexpr int PER_WAVE = kChunks * kBlock / 64 / W;   // 1 KiB copies per wave per tile
+  static_assert(W == 4, "exchange area sized for 4 waves");
+  static_assert(PER_WAVE * W * 64 == kChunks * kBlock, "tile must split evenly over waves");
+  static_assert((PER_WAVE * 64) % (16 * kChunks) == 0, "wave copy block must hold whole swizzle periods");
+  static_assert(PER_WAVE % NH == 0, "copies split over the halves");
+  static constexpr int FH = kDC / 16 / 2;                      // feature tiles per half (16)
+  static constexpr int KS = kDQ / 32;
+
+  const AttnParams& p;
+  int lane, wave, pair, fh, tg, col, grp;
+  int b, split, part, L, blk_lo, nb;
+  bool bad;
+  int qi, qh, n_vis;
+  bf16x8 qf[KS];
+  f32x4 acc_own[FH], acc_par[FH];   // rows of this wave's tile / of the partner's tile
+  float m_ref, l_run;               // this wave's tile
+  float qk_scale;
+  int s_base_even, s_base_odd;
+  int v_base[4];
+  uint32_t dma_off[PER_WAVE];
+
+  __device__ AbsorbPairCta(const AttnParams& p_) : p(p_) {}
+
+  __device__ __forceinline__ const char* tile_src(int k) const {
+    const int32_t id = max(g_ids[k], 0);
+    return static_cast<const char*>(p.kv) + static_cast<int64_t>(id) * kTileBytes + wave * PER_WAVE * 1024;
+  }
+  template <int BUF, int J>
+  __device__ __forceinline__ void issue_one(const char* src) {
+    copy16_to_lds(src + dma_off[J], (lds_void*)(tile_buf<BUF>() + (wave * PER_WAVE + J) * 1024));
+  }
+  template <int BUF, int J = 0>
+  __device__ __forceinline__ void issue_all(const char* src) {
+    if constexpr (J < PER_WAVE) {
+      issue_one<BUF, J>(src);
+      issue_all<BUF, J + 1>(src);
+    }
+  }
+  template <int BUF, int J0, int J = J0>
+  __device__ __forceinline__ void copy_at(int j, const char* src) {
+    if constexpr (J < PER_WAVE) {
+      if (j == J - J0) issue_one<BUF, J>(src);
+      else copy_at<BUF, J0, J + 1>(j, src);
+    }
+  }
+
+  template <int BUF>
+  __device__ __forceinline__ void clear_tail(int valid) {
+    char* tile = tile_buf<BUF>();
+    for (int i = valid * kChunks + threadIdx.x; i < kBlock * kChunks; i += W * 64)
+      *reinterpret_cast<uint4*>(tile + 16 * i) = uint4{0u, 0u, 0u, 0u};
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    lds_barrier();
+  }
+
+  // Scores S^T = C Q^T of tokens t0 .. t0+31 for this wave's tile, with copies
+  // J0 .. J0+CNT-1 of the next tile riding along (same scheme as AbsorbCta::score).
+  template <int BUF, int J0, int CNT>
+  __device__ __forceinline__ void score(int t0, f32x4 (&s)[2], const char* nxt) {
+    const char* tile = tile_buf<BUF>() + t0 * kRowBytes;
+    constexpr int N = 2 * KS;
+    constexpr int D = kScoreBatch;
+    static_assert(N % D == 0, "score batches");
+    auto ld = [&](int i) {
+      const int ks = i >> 1, tt = i & 1;
+      return *reinterpret_cast<const bf16x8*>(tile + tt * 16 * kRowBytes + ((ks & 1) ? s_base_odd : s_base_even) +
+                                              128 * (ks >> 1));
+    };
+    s[0] = s[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 a[N];
+#pragma unroll
+    for (int i = 0; i < D; ++i) a[i] = ld(i);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      s[i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], qf[i >> 1], s[i & 1], 0, 0, 0);
+      if (i % D == 0 && i + D < N) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) a[i + D + j] = ld(i + D + j);
+      }
+      constexpr int GAP = N / CNT;
+      if (i % GAP == GAP - 1 && i / GAP < CNT && nxt != nullptr) copy_at<1 - BUF, J0>(i / GAP, nxt);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // O^T += C^T P^T over tokens t0 .. t0+31 for latent features fh*256 .. +256 and both
+  // tiles of the pair: one transposed operand read per feature tile, two MFMAs.
+  template <int BUF>
+  __device__ __forceinline__ void value(int t0, bf16x8 p_own, bf16x8 p_par) {
+    const char* tile = tile_buf<BUF>() + t0 * kRowBytes + fh * 512;   // 128 B per 4 feature tiles
+    constexpr int D = kValueBatch;
+    static_assert(FH % D == 0, "value batches");
+    auto tr = [&](int ft, int second) {
+      return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(tile + v_base[ft & 3] + 128 * (ft >> 2) + second * 16 * kRowBytes));
+    };
+    i16x4 lo[FH], hi[FH];
+#pragma unroll
+    for (int ft = 0; ft < D; ++ft) { lo[ft] = tr(ft, 0); hi[ft] = tr(ft, 1); }
+#pragma unroll
+    for (int ft = 0; ft < FH; ++ft) {
+      const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo[ft], hi[ft], 0, 1, 2, 3, 4, 5, 6, 7));
+      acc_own[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, p_own, acc_own[ft], 0, 0, 0);
+      acc_par[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, p_par, acc_par[ft], 0, 0, 0);
+      if (ft % D == 0 && ft + D < FH) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) { lo[ft + D + j] = tr(ft + D + j, 0); hi[ft + D + j] = tr(ft + D + j, 1); }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  __device__ __forceinline__ char* xchg(int w) { return g_xchg + w * kXchgWave; }
+
+  template <int BUF>
+  __device__ __forceinline__ void step(int k) {
+    wait_vmcnt<0>();
+    lds_barrier();
+    if (k < nb) {
+      const int blk = blk_lo + k;
+      const char* nxt = k + 1 < nb ? tile_src(k + 1) : nullptr;
+      if ((blk + 1) * kBlock > L) clear_tail<BUF>(L - blk * kBlock);
+      // Scores of this wave's halves (h0 = the first one).
+      const int h0 = TG == 2 ? tg : 0;
+      f32x4 s[NH][2];
+      score<BUF, 0, PER_WAVE / NH>(h0 * 32, s[0], nxt);
+      if constexpr (NH == 2) score<BUF, PER_WAVE / 2, PER_WAVE / 2>(32, s[1], nxt);
+      // Online softmax over all of them: one max, lazy rescale (factor 1 when unchanged).
+      float sc[NH][8];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const int tb = blk * kBlock + (h0 + h) * 32 + 4 * grp;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int k2 = 0; k2 < 4; ++k2) {
+            const float v = (tb + 16 * tt + k2 < n_vis) ? s[h][tt][k2] * qk_scale : -INFINITY;
+            sc[h][4 * tt + k2] = v;
+            mx = fmaxf(mx, v);
+          }
+      }
+      mx = xor_max(mx);
+      float alpha = 1.f;
+      if (mx > m_ref + kRescaleSlack) {
+        alpha = __builtin_amdgcn_exp2f(m_ref - mx);
+        m_ref = mx;
+      }
+      l_run *= alpha;
+      const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+      bf16x8 pf[NH];
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float e = __builtin_amdgcn_exp2f(sc[h][j] - m_use);
+          l_run += e;
+          pf[h][j] = static_cast<__bf16>(e);
+        }
+      // Swap P^T operands and rescale factors with the partner wave.
+      char* mine = xchg(wave);
+#pragma unroll
+      for (int h = 0; h < NH; ++h) *reinterpret_cast<bf16x8*>(mine + h * 1024 + 16 * lane) = pf[h];
+      if (grp == 0) reinterpret_cast<float*>(mine + 2048)[col] = alpha;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      lds_barrier();
+      const char* theirs = xchg(wave ^ 1);
+      bf16x8 pp[NH];
+#pragma unroll
+      for (int h = 0; h < NH; ++h) pp[h] = *reinterpret_cast<const bf16x8*>(theirs + h * 1024 + 16 * lane);
+      const float alpha_par = reinterpret_cast<const float*>(theirs + 2048)[col];
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f || alpha_par != 1.f) != 0) {   // rare after the first block
+#pragma unroll
+        for (int ft = 0; ft < FH; ++ft) {
+          acc_own[ft] *= alpha;
+          acc_par[ft] *= alpha_par;
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < NH; ++h) value<BUF>((h0 + h) * 32, pf[h], pp[h]);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    lds_barrier();
+  }
+
+  __device__ __forceinline__ void run(int unit, int part_) {
+    part = part_;
+    lane = threadIdx.x & 63;
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    fh = wave & 1;
+    pair = (wave >> 1) % PR;
+    tg = (wave >> 1) / PR;
+    col = lane & 15;
+    grp = lane >> 4;
+    split = unit % p.n_split;
+    b = unit / p.n_split;
+    L = p.ctx_lens[b];
+    const int nblk = (L + kBlock - 1) / kBlock;
+    bad = (L < p.s_q) || (L > p.max_blocks * kBlock) || (nblk > p.n_split * p.blocks_per_split);
+    blk_lo = split * p.blocks_per_split;
+    const int blk_hi = bad ? blk_lo : min(nblk, blk_lo + p.blocks_per_split);
+    nb = max(0, blk_hi - blk_lo);
+    {
+      const int32_t* table = p.block_table + static_cast<int64_t>(b) * p.max_blocks + blk_lo;
+      for (int i = threadIdx.x; i < nb; i += W * 64) {
+        const int32_t id = table[i];
+        g_ids[i] = (id < 0 || id >= p.num_blocks) ? -1 : id;
+      }
+    }
+    // This wave scores tile 2*pair + fh: row = (part * RT + 2 * pair + fh) * 16 + col.
+    {
+      const int row = (part * RT + 2 * pair + fh) * 16 + col;
+      qi = row / p.H;
+      qh = row % p.H;
+      n_vis = L - p.s_q + 1 + qi;
+      const bf16_t* q = static_cast<const bf16_t*>(p.q) +
+                        (static_cast<int64_t>(b * p.s_q + qi) * p.H + qh) * kDQ + 8 * grp;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(q + 32 * ks);
+    }
+    m_ref = -INFINITY;
+    l_run = 0.f;
+#pragma unroll
+    for (int ft = 0; ft < FH; ++ft) acc_own[ft] = acc_par[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+    qk_scale = p.scale * kLog2e;
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) dma_off[j] = slot_source(j * 64 + lane);
+    {
+      const int sw = swz(col);
+      const int lo2 = (grp ^ sw) & 3;
+      s_base_even = col * kRowBytes + 16 * ((0 ^ (sw & 4)) | lo2);
+      s_base_odd = col * kRowBytes + 16 * ((4 ^ (sw & 4)) | lo2);
+      const int src = 4 * grp + (col >> 2);
+      const int sw2 = swz(src);
+      const int m4 = col & 3;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        v_base[q4] = src * kRowBytes + 16 * ((2 * q4 + (m4 >> 1)) ^ sw2) + 8 * (m4 & 1);
+    }
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    lds_barrier();
+    for (int i = 0; i < nb; ++i) bad |= g_ids[i] < 0;
+    nb = bad ? 0 : nb;
+    if (nb > 0) {
+      issue_all<0>(tile_src(0));
+      for (int k = 0; k < nb; k += 2) {
+        step<0>(k);
+        step<1>(k + 1);
+      }
+      wait_vmcnt<0>();
+      lds_barrier();
+    }
+
+    // Row statistics of every tile and token group: ml[tg][tile][16] (m, then l).
+    l_run = xor_sum(l_run);
+    float* ml = reinterpret_cast<float*>(g_xchg);
+    const int my_tile = 2 * pair + fh;
+    if (grp == 0) {
+      ml[((tg * RT + my_tile) * 2 + 0) * 16 + col] = m_ref;
+      ml[((tg * RT + my_tile) * 2 + 1) * 16 + col] = l_run;
+    }
+    // Token group 1 hands its accumulators to token group 0 (tile buffers are free now).
+    float* xo = reinterpret_cast<float*>(g_tile0);   // [pair][fh][own/par][FH][64 lanes][4]
+    auto xo_at = [&](int j, int ft) { return xo + ((((pair * 2 + fh) * 2 + j) * FH + ft) * 64 + lane) * 4; };
+    if (TG == 2 && tg == 1) {
+#pragma unroll
+      for (int ft = 0; ft < FH; ++ft) {
+        *reinterpret_cast<f32x4*>(xo_at(0, ft)) = acc_own[ft];
+        *reinterpret_cast<f32x4*>(xo_at(1, ft)) = acc_par[ft];
+      }
+    }
+    __syncthreads();
+    if (TG == 2 && tg == 1) return;
+    store_tile(acc_own, my_tile, 0, ml, xo_at, true);
+    store_tile(acc_par, 2 * pair + (fh ^ 1), 1, ml, xo_at, false);
+  }
+
+  // Merge (TG = 2) and store this wave's feature half of tile `tile` (rows of `acc`).
+  template <typename XO>
+  __device__ __forceinline__ void store_tile(f32x4 (&acc)[FH], int tile, int j, const float* ml, XO xo_at, bool lse_owner) {
+    float m = ml[((0 * RT + tile) * 2 + 0) * 16 + col];
+    float l = ml[((0 * RT + tile) * 2 + 1) * 16 + col];
+    if constexpr (TG == 2) {
+      const float m1 = ml[((1 * RT + tile) * 2 + 0) * 16 + col];
+      const float l1 = ml[((1 * RT + tile) * 2 + 1) * 16 + col];
+      const float M = fmaxf(m, m1);
+      const float M_use = (M == -INFINITY) ? 0.f : M;
+      const float w0 = __builtin_amdgcn_exp2f(m - M_use), w1 = __builtin_amdgcn_exp2f(m1 - M_use);
+#pragma unroll
+      for (int ft = 0; ft < FH; ++ft) acc[ft] = acc[ft] * w0 + *reinterpret_cast<const f32x4*>(xo_at(j, ft)) * w1;
+      l = l * w0 + l1 * w1;
+      m = M;
+    }
+    const int row = (part * RT + tile) * 16 + col;
+    const int qi_t = row / p.H, qh_t = row % p.H;
+    const int64_t orow = static_cast<int64_t>(b * p.s_q + qi_t) * p.H + qh_t;
+    const bool empty = !(l > 0.f);
+    const float inv = empty ? 0.f : 1.f / l;
+    float* dst = (p.n_split == 1 ? static_cast<float*>(p.out) + orow * kDC
+                                 : p.ws_o + (orow * p.n_split + split) * kDC) + fh * 256 + 4 * grp;
+#pragma unroll
+    for (int ft = 0; ft < FH; ++ft) {
+      f32x4 v = acc[ft] * inv;
+      if (bad) v = f32x4{nan_f32(), nan_f32(), nan_f32(), nan_f32()};
+      *reinterpret_cast<f32x4*>(dst + 16 * ft) = v;
+    }
+    if (lse_owner && grp == 0) {
+      const float lse = bad ? nan_f32() : (empty ? -INFINITY : (m + __log2f(l)) * kLn2);
+      if (p.n_split == 1) {
+        if (p.lse != nullptr) p.lse[orow] = lse;
+      } else {
+        p.ws_lse[orow * p.n_split + split] = lse;
+      }
+    }
+  }
+};
+
 // The H * s_q rows of a sequence are split into `parts` workgroups of RT * 16 rows. The
 // parts of one (sequence, split) unit get workgroup ids 8 apart, which the dispatcher
 // places on the same XCD, so each latent tile is read from HBM once and from that
@@ -479,6 +816,26 @@ hipError_t launch(const AttnParams& p, int parts, hipStream_t s) {
   const int64_t grid = parts == 1 ? units : ((units * parts + 8 * parts - 1) / (8 * parts)) * (8 * parts);
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   absorb_decode_split<RPW, RT, TG><<<static_cast<unsigned>(grid), RT / RPW * TG * 64, 0, s>>>(p, parts, static_cast<int>(units));
+  return hipGetLastError();
+}
+
+template <int RT, int TG>
+__global__ __launch_bounds__(RT * TG * 64, 1) void absorb_decode_pair(AttnParams p, int parts, int units) {
+  const int x = blockIdx.x & 7, y = blockIdx.x >> 3;
+  const int unit = parts == 1 ? static_cast<int>(blockIdx.x) : (y / parts) * 8 + x;
+  const int part = parts == 1 ? 0 : y % parts;
+  if (unit >= units) return;
+  AbsorbPairCta<RT, TG> cta(p);
+  cta.run(unit, part);
+}
+
+template <int RT, int TG>
+hipError_t launch_pair(const AttnParams& p, int parts, hipStream_t s) {
+  if (p.blocks_per_split > kMaxSplitBlocks) return hipErrorInvalidValue;
+  const int64_t units = static_cast<int64_t>(p.B) * p.n_split;
+  const int64_t grid = parts == 1 ? units : ((units * parts + 8 * parts - 1) / (8 * parts)) * (8 * parts);
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  absorb_decode_pair<RT, TG><<<static_cast<unsigned>(grid), RT * TG * 64, 0, s>>>(p, parts, static_cast<int>(units));
   return hipGetLastError();
 }
 
@@ -504,11 +861,13 @@ int tuned_absorb_max_blocks_per_split() { return kMaxSplitBlocks; }
 
 hipError_t launch_tuned_absorb(const AttnParams& p, const gqla_dims* d, hipStream_t s) {
   switch (d->num_heads * d->s_q) {
+    // At 32 rows the pair's extra exchange barrier costs more than the halved transposed
+    // reads save (measured 74 vs 71 us on LLaMA-3-8B batch 32); from 64 rows on the pair wins.
     case 16: return launch<1, 1, 2>(p, 1, s);
     case 32: return launch<1, 2, 2>(p, 1, s);
-    case 64: return launch<1, 4, 1>(p, 1, s);
-    case 128: return launch<1, 4, 1>(p, 2, s);
-    case 256: return launch<1, 4, 1>(p, 4, s);
+    case 64: return launch_pair<4, 1>(p, 1, s);
+    case 128: return launch_pair<4, 1>(p, 2, s);
+    case 256: return launch_pair<4, 1>(p, 4, s);
   }
   return hipErrorNotSupported;
 }
