@@ -292,11 +292,11 @@ struct AbsorbCta {
 
   // One 64-token block slot held in buffer BUF (k-th block of the split): wait for its
   // copy, then compute it while the copy of block k + 1 into the other buffer is issued
-  // piecemeal from inside the score loop. The other buffer is free: every wave passed the
-  // closing barrier of the previous step.
+  // piecemeal from inside the score loop. The other buffer is free: every wave has passed
+  // this step's opening barrier, so all of them are done reading it.
   template <int BUF>
   __device__ __forceinline__ void step(int k) {
-    wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(0);   // this block's copy has landed, this wave's LDS reads are done
     lds_barrier();
     if (k < nb) {
       const int blk = blk_lo + k;
@@ -310,8 +310,8 @@ struct AbsorbCta {
         half_step<BUF, PER_WAVE / 2, PER_WAVE / 2>(1, blk, nxt);
       }
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    lds_barrier();
+    // No closing barrier: the next step's opening barrier is passed only once every wave
+    // has finished this one, and the copy into this buffer is issued after it.
   }
 
   template <int BUF, int J0, int CNT>
@@ -594,7 +594,7 @@ struct AbsorbPairCta {
 
   template <int BUF>
   __device__ __forceinline__ void step(int k) {
-    wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(0);
     lds_barrier();
     if (k < nb) {
       const int blk = blk_lo + k;
@@ -659,8 +659,8 @@ struct AbsorbPairCta {
 #pragma unroll
       for (int h = 0; h < NH; ++h) value<BUF>((h0 + h) * 32, pf[h], pp[h]);
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    lds_barrier();
+    // No closing barrier (see AbsorbCta::step); the exchange area is rewritten only after
+    // the next opening barrier too.
   }
 
   __device__ __forceinline__ void run(int unit, int part_) {
