@@ -342,13 +342,22 @@ struct AbsorbCta {
     const int blk_hi = bad ? blk_lo : min(nblk, blk_lo + p.blocks_per_split);
     nb = max(0, blk_hi - blk_lo);
 
-    // Stage this split's block ids in LDS; -1 marks an id outside the pool.
-    {
-      const int32_t* table = p.block_table + static_cast<int64_t>(b) * p.max_blocks + blk_lo;
-      for (int i = threadIdx.x; i < nb; i += W * 64) {
-        const int32_t id = table[i];
-        g_ids[i] = (id < 0 || id >= p.num_blocks) ? -1 : id;
-      }
+    // The first tile's copy starts before the rest of the prologue; the block ids (staged
+    // in LDS, -1 marking an id outside the pool) and the queries load while it runs.
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) dma_off[j] = slot_source(j * 64 + lane);
+    const int32_t* table = p.block_table + static_cast<int64_t>(b) * p.max_blocks + blk_lo;
+    if (nb > 0) {
+      const int32_t id0 = table[0];
+      const int32_t c0 = (id0 < 0 || id0 >= p.num_blocks) ? 0 : id0;   // a bad id poisons the output anyway
+      issue_all<0>(static_cast<const char*>(p.kv) + static_cast<int64_t>(c0) * kTileBytes + wave * PER_WAVE * 1024);
+    }
+    constexpr int kIdsPerThread = kMaxSplitBlocks / (W * 64);
+    int32_t idr[kIdsPerThread];
+#pragma unroll
+    for (int u = 0; u < kIdsPerThread; ++u) {
+      const int i = threadIdx.x + u * W * 64;
+      idr[u] = i < nb ? table[i] : 0;
     }
 
     // Rows of this lane, one per row tile r: row = (part * RT + wr * RPW + r) * 16 + col,
@@ -369,8 +378,6 @@ struct AbsorbCta {
       for (int ft = 0; ft < FT; ++ft) acc[r][ft] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     qk_scale = p.scale * kLog2e;
-#pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) dma_off[j] = slot_source(j * 64 + lane);
     {
       const int sw = swz(col);
       const int lo2 = (grp ^ sw) & 3;
@@ -384,14 +391,19 @@ struct AbsorbCta {
         v_base[q4] = src * kRowBytes + 16 * ((2 * q4 + (m4 >> 1)) ^ sw2) + 8 * (m4 & 1);
     }
 
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");   // ids, queries and the first tile
+#pragma unroll
+    for (int u = 0; u < kIdsPerThread; ++u) {
+      const int i = threadIdx.x + u * W * 64;
+      if (i < nb) g_ids[i] = (idr[u] < 0 || idr[u] >= p.num_blocks) ? -1 : idr[u];
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     lds_barrier();
     for (int i = 0; i < nb; ++i) bad |= g_ids[i] < 0;   // uniform: every lane reads all ids
     const int nb_run = bad ? 0 : nb;
     nb = nb_run;
     // Blocks alternate buffers 0 and 1 in pairs.
     if (nb > 0) {
-      issue_all<0>(tile_src(0));
       for (int k = 0; k < nb; k += 2) {
         step<0>(k);
         step<1>(k + 1);
@@ -680,12 +692,22 @@ struct AbsorbPairCta {
     blk_lo = split * p.blocks_per_split;
     const int blk_hi = bad ? blk_lo : min(nblk, blk_lo + p.blocks_per_split);
     nb = max(0, blk_hi - blk_lo);
-    {
-      const int32_t* table = p.block_table + static_cast<int64_t>(b) * p.max_blocks + blk_lo;
-      for (int i = threadIdx.x; i < nb; i += W * 64) {
-        const int32_t id = table[i];
-        g_ids[i] = (id < 0 || id >= p.num_blocks) ? -1 : id;
-      }
+    // The first tile's copy starts before the rest of the prologue; the block ids (staged
+    // in LDS, -1 marking an id outside the pool) and the queries load while it runs.
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) dma_off[j] = slot_source(j * 64 + lane);
+    const int32_t* table = p.block_table + static_cast<int64_t>(b) * p.max_blocks + blk_lo;
+    if (nb > 0) {
+      const int32_t id0 = table[0];
+      const int32_t c0 = (id0 < 0 || id0 >= p.num_blocks) ? 0 : id0;   // a bad id poisons the output anyway
+      issue_all<0>(static_cast<const char*>(p.kv) + static_cast<int64_t>(c0) * kTileBytes + wave * PER_WAVE * 1024);
+    }
+    constexpr int kIdsPerThread = kMaxSplitBlocks / (W * 64);
+    int32_t idr[kIdsPerThread];
+#pragma unroll
+    for (int u = 0; u < kIdsPerThread; ++u) {
+      const int i = threadIdx.x + u * W * 64;
+      idr[u] = i < nb ? table[i] : 0;
     }
     // This wave scores tile 2*pair + fh: row = (part * RT + 2 * pair + fh) * 16 + col.
     {
@@ -703,8 +725,6 @@ struct AbsorbPairCta {
 #pragma unroll
     for (int ft = 0; ft < FH; ++ft) acc_own[ft] = acc_par[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
     qk_scale = p.scale * kLog2e;
-#pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) dma_off[j] = slot_source(j * 64 + lane);
     {
       const int sw = swz(col);
       const int lo2 = (grp ^ sw) & 3;
@@ -717,12 +737,17 @@ struct AbsorbPairCta {
       for (int q4 = 0; q4 < 4; ++q4)
         v_base[q4] = src * kRowBytes + 16 * ((2 * q4 + (m4 >> 1)) ^ sw2) + 8 * (m4 & 1);
     }
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");   // ids, queries and the first tile
+#pragma unroll
+    for (int u = 0; u < kIdsPerThread; ++u) {
+      const int i = threadIdx.x + u * W * 64;
+      if (i < nb) g_ids[i] = (idr[u] < 0 || idr[u] >= p.num_blocks) ? -1 : idr[u];
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     lds_barrier();
     for (int i = 0; i < nb; ++i) bad |= g_ids[i] < 0;
     nb = bad ? 0 : nb;
     if (nb > 0) {
-      issue_all<0>(tile_src(0));
       for (int k = 0; k < nb; k += 2) {
         step<0>(k);
         step<1>(k + 1);
