@@ -874,7 +874,7 @@ int absorb_parts(const gqla_dims* d) {
 bool tuned_absorb_supported(const gqla_dims* d) {
   const int rows = d->num_heads * d->s_q;
   return d->dtype == GQLA_BF16 && d->latent_rank == kDC && d->rope_dim == kDQ - kDC &&
-         (rows == 16 || rows == 32 || rows == 64 || rows == 128 || rows == 256);
+         (rows == 16 || rows == 32 || rows == 64 || rows == 128 || rows == 256 || rows == 512);
 }
 
 // One 156 KiB workgroup per CU; each (sequence, split) unit takes absorb_parts() of them.
@@ -893,6 +893,7 @@ hipError_t launch_tuned_absorb(const AttnParams& p, const gqla_dims* d, hipStrea
     case 64: return launch_pair<4, 1>(p, 1, s);
     case 128: return launch_pair<4, 1>(p, 2, s);
     case 256: return launch_pair<4, 1>(p, 4, s);
+    case 512: return launch_pair<4, 1>(p, 8, s);
   }
   return hipErrorNotSupported;
 }

@@ -57,19 +57,22 @@ __device__ __forceinline__ float xor_sum(float v) {
   return v + __shfl_xor(v, 32, 64);
 }
 
-template <int DQK, int DV, int kWaves>
+// RT = 16-row MFMA column tiles of query rows per group (gs * s_q <= 16 * RT); with two,
+// every K and V operand load feeds both tiles.
+template <int DQK, int DV, int kWaves, int RT>
 __global__ __launch_bounds__(kWaves * 64) void gqa_decode_split(AttnParams p) {
   constexpr int KS = DQK / 32;     // k-steps of the score product
   constexpr int NT = DV / 16;      // feature tiles of the value product
   constexpr int CHUNK = kBlock * (DQK + DV);
-  __shared__ float s_o[kWaves][NT][64][4];   // per-wave O^T fragments (lane-major)
-  __shared__ float s_m[kWaves][16];
-  __shared__ float s_l[kWaves][16];
+  constexpr bool kHalfUnits = RT == 2 && DQK > 128;
+  __shared__ float s_o[kWaves][RT][NT][64][4];   // per-wave O^T fragments (lane-major)
+  __shared__ float s_m[kWaves][RT * 16];
+  __shared__ float s_l[kWaves][RT * 16];
   __shared__ int s_bad[kWaves];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int col = lane & 15;          // query row owned by this lane (MFMA column)
+  const int col = lane & 15;          // query row owned by this lane in each tile (MFMA column)
   const int grp = lane >> 4;          // k-group of the MFMA operands
   const int split = blockIdx.x % p.n_split;
   const int bg = blockIdx.x / p.n_split;
@@ -82,29 +85,35 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_split(AttnParams p) {
   const int nblk = (L + kBlock - 1) / kBlock;
   bool bad = (L < p.s_q) || (L > p.max_blocks * kBlock) || (nblk > p.n_split * p.blocks_per_split);
 
-  // This lane's query row and its visible-token limit.
-  const int qi = col / gs;
-  const int qh = g * gs + col % gs;
-  const bool live_row = col < rows;
-  const int n_vis = live_row ? L - p.s_q + 1 + qi : L;
-
-  // B operand of S^T: Q^T slice (features 32*ks + 8*grp .. +8 of query row `col`).
-  bf16x8 qf[KS];
-  {
+  // This lane's query rows (one per tile) and their visible-token limits; B operand of S^T:
+  // Q^T slices (features 32*ks + 8*grp .. +8 of query row 16*r + col).
+  int n_vis[RT];
+  bf16x8 qf[RT][KS];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    const int j = 16 * r + col;
+    const int qi = j / gs;
+    const int qh = g * gs + j % gs;
+    const bool live_row = j < rows;
+    n_vis[r] = live_row ? L - p.s_q + 1 + qi : L;
     const bf16_t* q = static_cast<const bf16_t*>(p.q) +
                       (static_cast<int64_t>(b * p.s_q + qi) * p.H + qh) * DQK + 8 * grp;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      if (live_row) qf[ks] = load8(q + 32 * ks);
-      else qf[ks] = bf16x8{};
+      if (live_row) qf[r][ks] = load8(q + 32 * ks);
+      else qf[r][ks] = bf16x8{};
     }
   }
 
-  f32x4 acc[NT];
+  f32x4 acc[RT][NT];
+  float m_run[RT], l_run[RT];   // running max (log2 domain) and this lane's running sum
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;   // running max, log2 domain
-  float l_run = 0.f;         // running sum over this lane's tokens
+  for (int r = 0; r < RT; ++r) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[r][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[r] = -INFINITY;
+    l_run[r] = 0.f;
+  }
   const float qk_scale = p.scale * kLog2e;
 
   const bf16_t* kv = static_cast<const bf16_t*>(p.kv);
@@ -134,162 +143,191 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_split(AttnParams p) {
     return kv + (static_cast<int64_t>(id) * p.kv_heads + g) * CHUNK;
   };
 
-  // One block's operands: K rows of both 32-token halves, permuted so lane group `grp`
+  // One half block's operands: K rows of its 32 tokens, permuted so lane group `grp`
   // gets tokens 32*half + 8*grp .. +8, and V^T slices of the same tokens. K features
   // 32*ks .. +32 of all 64 tokens form one slab ([64][32]), V^T is stored as two 32-token
   // halves ([DV][32]): each load instruction reads four 256-byte runs of K or one 1 KiB
   // run of V^T.
-  struct Frag {
-    bf16x8 k[2][2][KS];
-    bf16x8 v[2][NT];
+  struct Half {
+    bf16x8 k[2][KS];
+    bf16x8 v[NT];
   };
-  auto load = [&](Frag& f, const bf16_t* chunk) {
+  auto load_half = [&](Half& f, const bf16_t* chunk, int half) {
     const bf16_t* vt = chunk + kBlock * DQK;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int tt = 0; tt < 2; ++tt) {
+      const int tok = 32 * half + 8 * (col >> 2) + 4 * tt + (col & 3);
+      const bf16_t* krow = chunk + tok * kSlab + 8 * grp;
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int tok = 32 * half + 8 * (col >> 2) + 4 * tt + (col & 3);
-        const bf16_t* krow = chunk + tok * kSlab + 8 * grp;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) f.k[half][tt][ks] = load8_stream(krow + ks * kBlock * kSlab);
-      }
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        f.v[half][nt] = load8_stream(vt + half * DV * kHalf + (16 * nt + col) * kHalf + 8 * grp);
+      for (int ks = 0; ks < KS; ++ks) f.k[tt][ks] = load8_stream(krow + ks * kBlock * kSlab);
     }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      f.v[nt] = load8_stream(vt + half * DV * kHalf + (16 * nt + col) * kHalf + 8 * grp);
   };
 
-  auto compute = [&](const Frag& f, int blk) {
+  auto compute_half = [&](const Half& f, int blk, int half) {
+    f32x4 s[RT][2];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      f32x4 s[2];
+    for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int r = 0; r < RT; ++r) s[r][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.k[half][tt][ks], qf[ks], s[tt], 0, 0, 0);
-      }
-      // Token of score s[tt][k] in this lane: blk*64 + 32*half + 8*grp + 4*tt + k.
-      const int tbase = blk * kBlock + 32 * half + 8 * grp;
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+          s[r][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.k[tt][ks], qf[r][ks], s[r][tt], 0, 0, 0);
+    }
+    // Token of score s[r][tt][k] in this lane: blk*64 + 32*half + 8*grp + 4*tt + k.
+    const int tbase = blk * kBlock + 32 * half + 8 * grp;
+    bf16x8 pf[RT];
+    float alpha[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
       float sc[8];
       float mx = -INFINITY;
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const float v = (tbase + 4 * tt + k < n_vis) ? s[tt][k] * qk_scale : -INFINITY;
+          const float v = (tbase + 4 * tt + k < n_vis[r]) ? s[r][tt][k] * qk_scale : -INFINITY;
           sc[4 * tt + k] = v;
           mx = fmaxf(mx, v);
         }
       mx = xor_max(mx);
-      const float m_new = fmaxf(m_run, mx);
+      const float m_new = fmaxf(m_run[r], mx);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      m_run = m_new;
+      alpha[r] = __builtin_amdgcn_exp2f(m_run[r] - m_use);
+      m_run[r] = m_new;
       float psum = 0.f;
-      bf16x8 pf;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const float e = __builtin_amdgcn_exp2f(sc[k] - m_use);
         psum += e;
-        pf[k] = static_cast<__bf16>(e);
+        pf[r][k] = static_cast<__bf16>(e);
       }
-      l_run = l_run * alpha + psum;
-      // Slots past the context hold arbitrary bits (possibly NaN): their value columns
-      // are masked to zero, two tokens per 32-bit word.
-      u32x4 keep = {~0u, ~0u, ~0u, ~0u};
-      if (blk * kBlock + kBlock > L) {
+      l_run[r] = l_run[r] * alpha[r] + psum;
+    }
+    // Slots past the context hold arbitrary bits (possibly NaN): their value columns
+    // are masked to zero, two tokens per 32-bit word.
+    u32x4 keep = {~0u, ~0u, ~0u, ~0u};
+    if (blk * kBlock + kBlock > L) {
 #pragma unroll
-        for (int w = 0; w < 4; ++w)
-          keep[w] = (tbase + 2 * w < L ? 0xffffu : 0u) | (tbase + 2 * w + 1 < L ? 0xffff0000u : 0u);
-      }
+      for (int w = 0; w < 4; ++w)
+        keep[w] = (tbase + 2 * w < L ? 0xffffu : 0u) | (tbase + 2 * w + 1 < L ? 0xffff0000u : 0u);
+    }
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const bf16x8 vm = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, f.v[half][nt]) & keep);
-        acc[nt] *= alpha;
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vm, pf, acc[nt], 0, 0, 0);
+    for (int nt = 0; nt < NT; ++nt) {
+      const bf16x8 vm = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, f.v[nt]) & keep);
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        acc[r][nt] *= alpha[r];
+        acc[r][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vm, pf[r], acc[r][nt], 0, 0, 0);
       }
     }
   };
 
-  // Two blocks in flight per wave: the next block's loads are issued before the current
-  // one is consumed. Past the last block the last one is fetched again (an L2 hit), so
-  // every iteration issues the same loads and the waits stay exact.
-  if (n_my > 0) {
-    Frag fa, fb;
-    load(fa, chunk_of(block_id(0)));
-    for (int j = 0; j < n_my; j += 2) {
-      load(fb, chunk_of(block_id(min(j + 1, n_my - 1))));
-      __builtin_amdgcn_sched_barrier(0);
-      compute(fa, first + kWaves * j);
-      load(fa, chunk_of(block_id(min(j + 2, n_my - 1))));
-      __builtin_amdgcn_sched_barrier(0);
-      if (j + 1 < n_my) compute(fb, first + kWaves * (j + 1));
+  if constexpr (!kHalfUnits) {
+    // Two blocks in flight per wave: the next block's loads are issued before the current
+    // one is consumed. Past the last block the last one is fetched again (an L2 hit), so
+    // every iteration issues the same loads and the waits stay exact.
+    auto load = [&](Half (&f)[2], const bf16_t* chunk) { load_half(f[0], chunk, 0); load_half(f[1], chunk, 1); };
+    auto compute = [&](const Half (&f)[2], int blk) { compute_half(f[0], blk, 0); compute_half(f[1], blk, 1); };
+    if (n_my > 0) {
+      Half fa[2], fb[2];
+      load(fa, chunk_of(block_id(0)));
+      for (int j = 0; j < n_my; j += 2) {
+        load(fb, chunk_of(block_id(min(j + 1, n_my - 1))));
+        __builtin_amdgcn_sched_barrier(0);
+        compute(fa, first + kWaves * j);
+        load(fa, chunk_of(block_id(min(j + 2, n_my - 1))));
+        __builtin_amdgcn_sched_barrier(0);
+        if (j + 1 < n_my) compute(fb, first + kWaves * (j + 1));
+      }
+    }
+  } else {
+    // Register budget of two row tiles at d_qk = 192: two half blocks in flight instead
+    // (the next half's loads issued before the current half is consumed).
+    if (n_my > 0) {
+      const int nu = 2 * n_my;
+      auto unit_chunk = [&](int u) { return chunk_of(block_id(min(u, nu - 1) >> 1)); };
+      Half fa, fb;
+      load_half(fa, unit_chunk(0), 0);
+      for (int u = 0; u < nu; u += 2) {
+        load_half(fb, unit_chunk(u + 1), 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_half(fa, first + kWaves * (u >> 1), 0);
+        load_half(fa, unit_chunk(u + 2), min(u + 2, nu - 1) & 1 ? 1 : 0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_half(fb, first + kWaves * (u >> 1), 1);
+      }
     }
   }
 
   // Merge the waves: O = sum_w 2^(m_w - M) O_w, l = sum_w 2^(m_w - M) l_w.
-  l_run = xor_sum(l_run);
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-    *reinterpret_cast<f32x4*>(&s_o[wave][nt][lane][0]) = acc[nt];
-  if (grp == 0) { s_m[wave][col] = m_run; s_l[wave][col] = l_run; }
+  for (int r = 0; r < RT; ++r) {
+    l_run[r] = xor_sum(l_run[r]);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      *reinterpret_cast<f32x4*>(&s_o[wave][r][nt][lane][0]) = acc[r][nt];
+    if (grp == 0) { s_m[wave][16 * r + col] = m_run[r]; s_l[wave][16 * r + col] = l_run[r]; }
+  }
   if (lane == 0) s_bad[wave] = bad;
   __syncthreads();
-  // The first 256 threads write: thread -> (query row jr, 8 consecutive features).
-  if (threadIdx.x >= 16 * (DV / 8)) return;
-
   bool any_bad = false;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) any_bad |= s_bad[w] != 0;
-  const int jr = threadIdx.x >> 4;
-  const int f0 = (threadIdx.x & 15) * 8;
-  float M = -INFINITY;
+  // Thread -> (query row jr, 8 consecutive features), 16 threads per row.
+  for (int item = threadIdx.x; item < 16 * RT * (DV / 8); item += kWaves * 64) {
+    const int jr = item / (DV / 8);
+    const int f0 = (item % (DV / 8)) * 8;
+    if (jr >= rows) break;   // items are row-major, so every later one is past the rows too
+    const int r = jr >> 4, c = jr & 15;
+    float M = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][jr]);
-  const float M_use = (M == -INFINITY) ? 0.f : M;
-  float wgt[kWaves];
-  float l_tot = 0.f;
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][jr]);
+    const float M_use = (M == -INFINITY) ? 0.f : M;
+    float wgt[kWaves];
+    float l_tot = 0.f;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    wgt[w] = __builtin_amdgcn_exp2f(s_m[w][jr] - M_use);
-    l_tot += wgt[w] * s_l[w][jr];
-  }
-  float o[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    // feature f = f0 + k lives in tile f/16, lane (jr + 16 * ((f % 16) / 4)), slot f % 4
-    const int f = f0 + k;
-    const int ln = jr + 16 * ((f & 15) >> 2);
-    float v = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) v += wgt[w] * s_o[w][f >> 4][ln][f & 3];
-    o[k] = v;
-  }
-  if (jr >= rows) return;
-  const int i = jr / gs;
-  const int h = g * gs + jr % gs;
-  const int64_t row = static_cast<int64_t>(b * p.s_q + i) * p.H + h;
-  if (p.n_split == 1) {
-    const float inv = 1.f / l_tot;
-    bf16_t packed[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) packed[k] = any_bad ? 0x7fc0 : f32_to_bf16(o[k] * inv);
-    *reinterpret_cast<uint4*>(static_cast<bf16_t*>(p.out) + row * DV + f0) = *reinterpret_cast<uint4*>(packed);
-    if (p.lse != nullptr && f0 == 0) p.lse[row] = any_bad ? nan_f32() : (M + __log2f(l_tot)) * kLn2;
-  } else {
-    const int64_t slot = row * p.n_split + split;
-    const bool empty = !(l_tot > 0.f);
-    float* dst = p.ws_o + slot * DV + f0;
-#pragma unroll
-    for (int k = 0; k < 8; k += 4) {
-      f32x4 v;
-      for (int u = 0; u < 4; ++u) v[u] = any_bad ? nan_f32() : (empty ? 0.f : o[k + u] / l_tot);
-      *reinterpret_cast<f32x4*>(dst + k) = v;
+    for (int w = 0; w < kWaves; ++w) {
+      wgt[w] = __builtin_amdgcn_exp2f(s_m[w][jr] - M_use);
+      l_tot += wgt[w] * s_l[w][jr];
     }
-    if (f0 == 0) p.ws_lse[slot] = any_bad ? nan_f32() : (empty ? -INFINITY : (M + __log2f(l_tot)) * kLn2);
+    float o[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      // feature f = f0 + k lives in tile f/16, lane (c + 16 * ((f % 16) / 4)), slot f % 4
+      const int f = f0 + k;
+      const int ln = c + 16 * ((f & 15) >> 2);
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) v += wgt[w] * s_o[w][r][f >> 4][ln][f & 3];
+      o[k] = v;
+    }
+    const int i = jr / gs;
+    const int h = g * gs + jr % gs;
+    const int64_t row = static_cast<int64_t>(b * p.s_q + i) * p.H + h;
+    if (p.n_split == 1) {
+      const float inv = 1.f / l_tot;
+      bf16_t packed[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) packed[k] = any_bad ? 0x7fc0 : f32_to_bf16(o[k] * inv);
+      *reinterpret_cast<uint4*>(static_cast<bf16_t*>(p.out) + row * DV + f0) = *reinterpret_cast<uint4*>(packed);
+      if (p.lse != nullptr && f0 == 0) p.lse[row] = any_bad ? nan_f32() : (M + __log2f(l_tot)) * kLn2;
+    } else {
+      const int64_t slot = row * p.n_split + split;
+      const bool empty = !(l_tot > 0.f);
+      float* dst = p.ws_o + slot * DV + f0;
+#pragma unroll
+      for (int k = 0; k < 8; k += 4) {
+        f32x4 v;
+        for (int u = 0; u < 4; ++u) v[u] = any_bad ? nan_f32() : (empty ? 0.f : o[k + u] / l_tot);
+        *reinterpret_cast<f32x4*>(dst + k) = v;
+      }
+      if (f0 == 0) p.ws_lse[slot] = any_bad ? nan_f32() : (empty ? -INFINITY : (M + __log2f(l_tot)) * kLn2);
+    }
   }
 }
 
@@ -298,7 +336,7 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_split(AttnParams p) {
 bool tuned_gqa_supported(const gqla_dims* d) {
   const int dqk = d->nope_dim + d->rope_dim;
   const int gs = d->num_heads / d->num_groups;
-  return d->dtype == GQLA_BF16 && (dqk == 128 || dqk == 192) && d->v_dim == 128 && gs * d->s_q <= 16;
+  return d->dtype == GQLA_BF16 && (dqk == 128 || dqk == 192) && d->v_dim == 128 && gs * d->s_q <= 32;
 }
 
 // One 4-wave workgroup per CU per round: on MI355X the unsplit launch streams fastest
@@ -307,17 +345,19 @@ bool tuned_gqa_supported(const gqla_dims* d) {
 int tuned_gqa_target_wgs() { return kNumCUs; }
 int tuned_gqa_min_blocks_per_split() { return 8; }
 
-template <int DQK>
+template <int DQK, int RT>
 hipError_t launch_dqk(const AttnParams& p, int64_t wgs, hipStream_t s) {
   constexpr int kWaves = 4;
-  gqa_decode_split<DQK, 128, kWaves><<<static_cast<unsigned>(wgs), kWaves * 64, 0, s>>>(p);
+  gqa_decode_split<DQK, 128, kWaves, RT><<<static_cast<unsigned>(wgs), kWaves * 64, 0, s>>>(p);
   return hipGetLastError();
 }
 
 hipError_t launch_tuned_gqa(const AttnParams& p, const gqla_dims* d, hipStream_t s) {
   const int64_t wgs = static_cast<int64_t>(p.B) * p.kv_heads * p.n_split;
   if (wgs > 0x7fffffff) return hipErrorInvalidConfiguration;
-  return d->nope_dim + d->rope_dim == 192 ? launch_dqk<192>(p, wgs, s) : launch_dqk<128>(p, wgs, s);
+  const bool two = p.heads_per_kv * p.s_q > 16;
+  if (d->nope_dim + d->rope_dim == 192) return two ? launch_dqk<192, 2>(p, wgs, s) : launch_dqk<192, 1>(p, wgs, s);
+  return two ? launch_dqk<128, 2>(p, wgs, s) : launch_dqk<128, 1>(p, wgs, s);
 }
 
 }  // namespace gqla

@@ -13,8 +13,11 @@ from gpu_util import (TOL, Run, expanded_to_logical, log, logical_to_expanded, o
 
 pytestmark = pytest.mark.gpu
 
+# gs * s_q = 4, 8, 8, 16, 16 rows per group; s_q = 4 at gs = 8 and s_q = 8 at gs = 4 give
+# 32 rows, i.e. two MFMA row tiles (the d_qk = 192 one with half-block load units).
 SHAPES = [("llama3-8b-b32-ctx8k", 1), ("llama3-8b-b32-ctx8k", 2), ("dsv3-b64-ctx8k", 1),
-          ("dsv3-b64-ctx8k", 2), ("dsv3-tp8share-ctx16k", 2)]
+          ("dsv3-b64-ctx8k", 2), ("dsv3-tp8share-ctx16k", 2), ("dsv3-b64-ctx8k", 4),
+          ("llama3-8b-b32-ctx8k", 8)]
 
 
 def _ctx(s_q):
@@ -84,7 +87,8 @@ def test_paths_agree_on_gpu(name, s_q):
 
 
 ABSORB_SHAPES = [("llama3-8b-b32-ctx8k", 1), ("llama3-8b-b32-ctx8k", 2), ("dsv3-b64-ctx8k", 1),
-                 ("dsv3-b64-ctx8k", 2), ("dsv3-tp8share-ctx16k", 1), ("dsv3-tp8share-ctx16k", 2)]
+                 ("dsv3-b64-ctx8k", 2), ("dsv3-tp8share-ctx16k", 1), ("dsv3-tp8share-ctx16k", 2),
+                 ("dsv3-b64-ctx8k", 4)]
 
 
 @pytest.mark.parametrize("name,s_q", ABSORB_SHAPES)
