@@ -21,7 +21,7 @@ GQLA_PATH_ABSORB, GQLA_PATH_GQA = 0, 1
 EXPORTED = ("gqla_absorb_query", "gqla_decode_absorb", "gqla_out_proj", "gqla_expand_cache",
             "gqla_decode_gqa", "gqla_num_splits", "gqla_workspace_bytes",
             "gqla_cache_bytes_per_token", "gqla_validate_paged", "gqla_status_string",
-            "gqla_last_error", "gqla_version")
+            "gqla_last_error", "gqla_version", "gqla_pick_path")
 
 
 class GqlaError(RuntimeError):
@@ -61,6 +61,7 @@ def _load() -> ctypes.CDLL:
         "gqla_num_splits": [D, P, i32, ctypes.POINTER(i32)],
         "gqla_workspace_bytes": [D, P, i32, ctypes.POINTER(sz)],
         "gqla_validate_paged": [D, P, vp],
+        "gqla_pick_path": [D, i64, i32, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_float)],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -197,6 +198,16 @@ def gqla_workspace_bytes(dims: Dims, path: int, max_blocks: int, max_ctx_len: in
 def gqla_cache_bytes_per_token(dims: Dims, path: int) -> int:
     d = dims.c()
     return LIB.gqla_cache_bytes_per_token(ctypes.byref(d), path)
+
+
+def gqla_pick_path(dims: Dims, total_ctx: int, max_ctx: int):
+    """(path, (absorb_us, gqa_us)): the decode path the MI355X cost model picks."""
+    d = dims.c()
+    path = ctypes.c_int32()
+    est = (ctypes.c_float * 2)()
+    _check(LIB.gqla_pick_path(ctypes.byref(d), ctypes.c_int64(total_ctx), ctypes.c_int32(max_ctx),
+                              ctypes.byref(path), est), "gqla_pick_path")
+    return path.value, (float(est[0]), float(est[1]))
 
 
 def gqla_validate_paged(dims: Dims, paged: Paged, stream=None) -> None:

@@ -353,4 +353,27 @@ const char* gqla_last_error(void) { return g_err.c_str(); }
 
 const char* gqla_version(void) { return "gqla-mi355x 0.1 (gfx950)"; }
 
+gqla_status gqla_pick_path(const gqla_dims* dims, int64_t total_ctx, int32_t max_ctx, int32_t* path, float* est_us) {
+  gqla_status st = check_dims(dims);
+  if (st != GQLA_OK) return st;
+  if (path == nullptr) return fail(GQLA_ERR_INVALID_ARG, "path is NULL");
+  if (max_ctx < dims->s_q) return fail(GQLA_ERR_INVALID_ARG, "max_ctx (%d) must be >= s_q (%d)", max_ctx, dims->s_q);
+  if (total_ctx < static_cast<int64_t>(dims->batch) * dims->s_q ||
+      total_ctx > static_cast<int64_t>(dims->batch) * max_ctx)
+    return fail(GQLA_ERR_INVALID_ARG, "total_ctx (%lld) must lie in [batch * s_q, batch * max_ctx]",
+                static_cast<long long>(total_ctx));
+  gqla_paged pg{};
+  pg.max_ctx_len = max_ctx;
+  pg.max_blocks_per_seq = (max_ctx + gqla::kBlock - 1) / gqla::kBlock;
+  pg.num_blocks = 1;
+  const gqla::PathEstimate e =
+      gqla::estimate_paths(dims, total_ctx, plan(dims, &pg, GQLA_PATH_ABSORB).n_split, plan(dims, &pg, GQLA_PATH_GQA).n_split);
+  *path = e.gqa_us < e.absorb_us ? GQLA_PATH_GQA : GQLA_PATH_ABSORB;
+  if (est_us != nullptr) {
+    est_us[0] = static_cast<float>(e.absorb_us);
+    est_us[1] = static_cast<float>(e.gqa_us);
+  }
+  return GQLA_OK;
+}
+
 }  // extern "C"

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
+struct gqla_dims;   // include/gqla.h
+
 namespace gqla {
 
 constexpr int kBlock = 64;        // tokens per cache block
@@ -65,5 +67,11 @@ hipError_t launch_generic_out_proj(const ProjParams& d, const float* o_lat, cons
 hipError_t launch_generic_expand(const ProjParams& d, const void* latent, const void* w_uk,
                                  const void* w_uv, const int32_t* block_ids, int64_t n_blocks,
                                  int64_t num_blocks, void* expanded, bool bf16, hipStream_t s);
+
+// Decode-step estimate of each path (microseconds) on MI355X; path_model.cpp.
+struct PathEstimate {
+  double absorb_us, gqa_us;
+};
+PathEstimate estimate_paths(const ::gqla_dims* d, int64_t total_ctx, int n_split_abs, int n_split_gqa);
 
 }  // namespace gqla

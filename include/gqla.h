@@ -180,6 +180,26 @@ gqla_status gqla_num_splits(const gqla_dims* dims, const gqla_paged* paged, int3
 gqla_status gqla_workspace_bytes(const gqla_dims* dims, const gqla_paged* paged, int32_t path,
                                  size_t* bytes);
 
+/*
+ * gqla_pick_path — which decode path to run for a batch on MI355X (host arithmetic only).
+ * The two paths compute the same attention ("GQLA: Attention latente ...", English abstract:
+ * GQLA decodes either as MQA-absorb or as GQA; gqla_attn.py's decode_path switch), but trade
+ * cache traffic for computation, so the faster one depends on the hardware. This returns
+ * the path whose estimated decode step (absorbed query + latent decode + value projection,
+ * against expansion of the new tokens' blocks + grouped decode, each with its split
+ * combine) is shorter, from the per-step bytes and flops of these kernels and throughputs
+ * measured for them on MI355X. Ties go to the absorb path (the smaller cache).
+ *   total_ctx : sum of the batch's context lengths (each includes its s_q new tokens)
+ *   max_ctx   : longest context in the batch
+ *   path      : (output) GQLA_PATH_ABSORB or GQLA_PATH_GQA
+ *   est_us    : (output, NULL = skip) float[2]: estimated step microseconds {absorb, gqa}
+ * Errors: GQLA_ERR_INVALID_ARG for bad dims or total_ctx outside [B * s_q, B * max_ctx].
+ * The GQA path also needs the expanded cache, G * (d_qk + d_v) values per token: the
+ * caller decides whether that fits (gqla_cache_bytes_per_token).
+ */
+gqla_status gqla_pick_path(const gqla_dims* dims, int64_t total_ctx, int32_t max_ctx, int32_t* path,
+                           float* est_us);
+
 /* Cache bytes per token per layer: latent (d_c + d_R) * elt for the absorb path,
  * G * (d_qk + d_v) * elt for the GQA path; 0 for invalid arguments. */
 int64_t gqla_cache_bytes_per_token(const gqla_dims* dims, int32_t path);
