@@ -244,6 +244,19 @@ def main():
     t_gqa = np.mean([m[2].elapsed_time(m[3]) for m in marks])
     log(f"[bench] ms/step {ms_step:.4f}: expand {t_exp:.4f} absorb {t_abs:.4f} gqa {t_gqa:.4f}")
 
+    # The append path (not part of the step): the s_q GQA-path tokens of every sequence
+    # written into the latent cache with their rotated keys and expanded into the groups.
+    c_app = torch.randn(B, a.gqa_sq, w.latent, device="cuda").to(torch.bfloat16)
+    kr_app = torch.randn(B, a.gqa_sq, w.rope, device="cuda").to(torch.bfloat16)
+    G.gqla_append_tokens(d_gqa, paged, c_app, kr_app, 10000.0, w_uk, w_uv, cache, expanded)
+    e0, e1 = E(), E()
+    e0.record()
+    for _ in range(a.steps):
+        G.gqla_append_tokens(d_gqa, paged, c_app, kr_app, 10000.0, w_uk, w_uv, cache, expanded)
+    e1.record()
+    torch.cuda.synchronize()
+    t_app = e0.elapsed_time(e1) / a.steps
+
     ctx = x.ctx_lens.astype(np.int64)
     elt = 2
     kv_abs = float(ctx.sum() * (w.latent + w.rope) * elt)
@@ -274,6 +287,7 @@ def main():
                     "hbm_frac": kv_gqa / (t_gqa / 1e3) / 1e9 / HBM_PEAK_GBS,
                     "flops": fl_gqa, "mfma_frac": fl_gqa / (t_gqa / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
             "expand_tail": {"blocks": int(tail_ids.numel()), "ms": t_exp},
+            "append": {"tokens": B * a.gqa_sq, "ms": t_app, "note": "gqla_append_tokens with expansion, timed apart from the step"},
         },
         "roofline": {"kernel": "gqa_decode_split (gqla_decode_gqa)", "bound": "hbm",
                      "achieved": kv_gqa / (t_gqa / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",

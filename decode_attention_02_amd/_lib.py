@@ -21,7 +21,7 @@ GQLA_PATH_ABSORB, GQLA_PATH_GQA = 0, 1
 EXPORTED = ("gqla_absorb_query", "gqla_decode_absorb", "gqla_out_proj", "gqla_expand_cache",
             "gqla_decode_gqa", "gqla_num_splits", "gqla_workspace_bytes",
             "gqla_cache_bytes_per_token", "gqla_validate_paged", "gqla_status_string",
-            "gqla_last_error", "gqla_version", "gqla_pick_path")
+            "gqla_last_error", "gqla_version", "gqla_pick_path", "gqla_append_tokens")
 
 
 class GqlaError(RuntimeError):
@@ -62,6 +62,7 @@ def _load() -> ctypes.CDLL:
         "gqla_workspace_bytes": [D, P, i32, ctypes.POINTER(sz)],
         "gqla_validate_paged": [D, P, vp],
         "gqla_pick_path": [D, i64, i32, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_float)],
+        "gqla_append_tokens": [D, P, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -198,6 +199,14 @@ def gqla_workspace_bytes(dims: Dims, path: int, max_blocks: int, max_ctx_len: in
 def gqla_cache_bytes_per_token(dims: Dims, path: int) -> int:
     d = dims.c()
     return LIB.gqla_cache_bytes_per_token(ctypes.byref(d), path)
+
+
+def gqla_append_tokens(dims: Dims, paged: Paged, c_new, kr_new, rope_theta: float, w_uk, w_uv, latent_cache,
+                       expanded_cache=None, stream=None) -> None:
+    d, p = dims.c(), paged.c()
+    _check(LIB.gqla_append_tokens(ctypes.byref(d), ctypes.byref(p), _ptr(c_new), _ptr(kr_new), ctypes.c_float(rope_theta),
+                                  _ptr(w_uk), _ptr(w_uv), _ptr(latent_cache), _ptr(expanded_cache), _stream(stream)),
+           "gqla_append_tokens")
 
 
 def gqla_pick_path(dims: Dims, total_ctx: int, max_ctx: int):

@@ -376,4 +376,38 @@ gqla_status gqla_pick_path(const gqla_dims* dims, int64_t total_ctx, int32_t max
   return GQLA_OK;
 }
 
+gqla_status gqla_append_tokens(const gqla_dims* dims, const gqla_paged* paged, const void* c_new,
+                               const void* kr_new, float rope_theta, const void* w_uk, const void* w_uv,
+                               void* latent_cache, void* expanded_cache, void* stream) {
+  gqla_status st = check_dims(dims);
+  if (st != GQLA_OK) return st;
+  if ((st = check_paged(dims, paged)) != GQLA_OK) return st;
+  if (!c_new || !latent_cache || (dims->rope_dim > 0 && !kr_new))
+    return fail(GQLA_ERR_INVALID_ARG, "null tensor pointer");
+  if (expanded_cache && (!w_uk || !w_uv)) return fail(GQLA_ERR_INVALID_ARG, "expansion needs w_uk and w_uv");
+  if (!(rope_theta > 0.f)) return fail(GQLA_ERR_INVALID_ARG, "rope_theta must be > 0");
+  if (dims->rope_dim % 2 != 0) return fail(GQLA_ERR_INVALID_ARG, "rope_dim must be even (rotation pairs)");
+  if (dims->latent_rank % 8 != 0) return fail(GQLA_ERR_UNSUPPORTED, "append needs latent_rank % 8 == 0");
+  if (static_cast<int64_t>(16) * (dims->latent_rank + dims->rope_dim) * 4 > 160 * 1024)
+    return fail(GQLA_ERR_UNSUPPORTED, "latent row too wide for the append kernel's LDS tile");
+  const int64_t n_tok = static_cast<int64_t>(dims->batch) * dims->s_q;
+  if (n_tok > 0x7fffffff) return fail(GQLA_ERR_INVALID_ARG, "too many new tokens");
+  gqla::AppendParams a{};
+  a.block_table = paged->block_table;
+  a.ctx_lens = paged->ctx_lens;
+  a.max_blocks = paged->max_blocks_per_seq;
+  a.num_blocks = paged->num_blocks;
+  a.n_tok = static_cast<int32_t>(n_tok);
+  a.s_q = dims->s_q;
+  a.G = dims->num_groups;
+  a.dc = dims->latent_rank;
+  a.dr = dims->rope_dim;
+  a.dn = dims->nope_dim;
+  a.dv = dims->v_dim;
+  a.rope_theta = rope_theta;
+  hipError_t e = gqla::launch_append(a, c_new, kr_new, w_uk, w_uv, latent_cache, expanded_cache,
+                                     dims->dtype == GQLA_BF16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GQLA_OK : hip_fail(e, "append launch");
+}
+
 }  // extern "C"

@@ -68,6 +68,19 @@ hipError_t launch_generic_expand(const ProjParams& d, const void* latent, const 
                                  const void* w_uv, const int32_t* block_ids, int64_t n_blocks,
                                  int64_t num_blocks, void* expanded, bool bf16, hipStream_t s);
 
+// One append call: the s_q new tokens of every sequence (n_tok = B * s_q).
+struct AppendParams {
+  const int32_t* block_table;
+  const int32_t* ctx_lens;
+  int32_t max_blocks;
+  int64_t num_blocks;
+  int32_t n_tok, s_q, G;
+  int32_t dc, dr, dn, dv;
+  float rope_theta;
+};
+hipError_t launch_append(const AppendParams& a, const void* c_new, const void* kr_new, const void* w_uk,
+                         const void* w_uv, void* latent, void* expanded, bool bf16, hipStream_t s);
+
 // Decode-step estimate of each path (microseconds) on MI355X; path_model.cpp.
 struct PathEstimate {
   double absorb_us, gqa_us;

@@ -172,6 +172,30 @@ gqla_status gqla_decode_gqa(const gqla_dims* dims, const gqla_paged* paged, cons
                             const void* expanded_cache, void* workspace, size_t workspace_bytes,
                             void* out, float* lse, void* stream);
 
+/*
+ * gqla_append_tokens — write each sequence's s_q new tokens into the paged caches (the
+ * step before decode: the latent comes out of the down-projection and, on the GQA path,
+ * is expanded into the groups' K/V — "GQLA: Attention latente ...", English abstract;
+ * gqla_attn.py docstring). For row i of sequence b, at position t = L_b - s_q + i:
+ *   latent_cache[block_table[b][t / 64]][t % 64] = [ c_new[b][i] ; RoPE_t(kr_new[b][i]) ]
+ * and, when expanded_cache is not NULL, that slot's K and V for every group, as
+ * gqla_expand_cache would write them from the new latent row. RoPE pairs component k with
+ * k + d_R/2 and rotates the pair by t * rope_theta^(-2k/d_R) (computed in fp64, rounded
+ * once to the data type); the pages do not describe RoPE, this is the half-split form.
+ *   c_new          : data [B][s_q][d_c]
+ *   kr_new         : data [B][s_q][d_R], not yet rotated (may be NULL when d_R = 0)
+ *   rope_theta     : > 0 (10000 for the workloads here)
+ *   w_uk, w_uv     : data [G][d_n][d_c], [G][d_v][d_c] (needed only with expanded_cache)
+ *   latent_cache   : data [num_blocks][64][d_c + d_R] (updated in place)
+ *   expanded_cache : layout of gqla_expand_cache, or NULL for an absorb-only deployment
+ * Sequences with s_q > L_b or L_b beyond the table, and tokens whose block id lies outside
+ * [0, num_blocks), are skipped (nothing written). Requires d_R even, d_c % 8 == 0 and
+ * 64 * (d_c + d_R) <= 160 KiB; errors: GQLA_ERR_INVALID_ARG / GQLA_ERR_UNSUPPORTED.
+ */
+gqla_status gqla_append_tokens(const gqla_dims* dims, const gqla_paged* paged, const void* c_new,
+                               const void* kr_new, float rope_theta, const void* w_uk, const void* w_uv,
+                               void* latent_cache, void* expanded_cache, void* stream);
+
 /* Number of KV splits the decode call for `path` will use (host arithmetic only). */
 gqla_status gqla_num_splits(const gqla_dims* dims, const gqla_paged* paged, int32_t path,
                             int32_t* n);

@@ -239,6 +239,45 @@ def expand_blocks(latent_cache, block_ids, w_uk, w_uv, d_c):
     return np.array(Ks), np.array(Vs)
 
 
+# ------------------------------------------------------------------- append path
+
+def rope_at(x, position, theta=10000.0):
+    """Rotary position embedding of one d_R-vector at an integer position.
+
+    The pages never describe RoPE; reading: half-split pairs, i.e. component k is paired
+    with component k + d_R/2 and the pair is rotated by the angle
+    position * theta**(-2k/d_R) (x_k cos - x_{k+d/2} sin, x_k sin + x_{k+d/2} cos).
+    """
+    d = len(x)
+    half = d // 2
+    out = np.zeros(d)
+    for k in range(half):
+        angle = position * theta ** (-2.0 * k / d)
+        c, s = math.cos(angle), math.sin(angle)
+        out[k] = x[k] * c - x[k + half] * s
+        out[k + half] = x[k] * s + x[k + half] * c
+    return out
+
+
+def append_rows(c_new, kr_new, ctx_lens, s_q, theta=10000.0):
+    """Cache rows that appending each sequence's s_q new tokens writes: row i of sequence
+    b sits at position t = L_b - s_q + i (the context counts the new tokens) and is stored
+    as [c ; RoPE_t(k_rope)] (the latent from the down-projection plus the rotated
+    decoupled key, cached once per token for all heads).
+
+    c_new [B][s_q][d_c], kr_new [B][s_q][d_R] -> {(b, t): row [d_c + d_R]}.
+    """
+    rows = {}
+    for b in range(len(ctx_lens)):
+        L = int(ctx_lens[b])
+        if L < s_q:
+            continue
+        for i in range(s_q):
+            t = L - s_q + i
+            rows[(b, t)] = np.concatenate([c_new[b, i], rope_at(kr_new[b, i], t, theta)])
+    return rows
+
+
 # ----------------------------------------------------------- split-KV partial merge
 
 def merge_partials(outs: Sequence[np.ndarray], lses: Sequence[float]):

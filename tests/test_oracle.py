@@ -352,3 +352,41 @@ def test_pins_catch_planted_mistakes(mistake):
             return out
         M = _mutant(out_projection=out_projection)
     assert not _pins_pass(M)
+
+
+# ------------------------------------------------------------------ append-path pins
+
+def test_rope_at_worked_values():
+    """RoPE closed forms (reading: half-split pairs, theta 10000). With d_R = 2 the single
+    pair turns by the position itself; with d_R = 4, component 0 pairs with 2 (not 1) and
+    the second pair turns at theta^(-1/2) = 1/100 of the rate."""
+    t = 3.0
+    assert np.allclose(R.rope_at(np.array([1.0, 0.0]), t), [math.cos(t), math.sin(t)], atol=1e-15)
+    assert np.allclose(R.rope_at(np.array([1.0, 0.0, 0.0, 0.0]), t), [math.cos(t), 0, math.sin(t), 0], atol=1e-15)
+    assert np.allclose(R.rope_at(np.array([0.0, 1.0, 0.0, 0.0]), t),
+                       [0, math.cos(t / 100), 0, math.sin(t / 100)], atol=1e-15)
+
+
+def test_rope_at_is_a_relative_rotation():
+    """Position 0 is the identity, norms are kept, and <R_m q, R_n k> depends on m - n only
+    (the defining property of rotary embeddings)."""
+    rng = np.random.default_rng(5)
+    q, k = rng.standard_normal(64), rng.standard_normal(64)
+    assert np.array_equal(R.rope_at(q, 0), q)
+    assert math.isclose(np.linalg.norm(R.rope_at(q, 12345)), np.linalg.norm(q), rel_tol=1e-12)
+    a = R.rope_at(q, 700) @ R.rope_at(k, 300)
+    b = R.rope_at(q, 400) @ k
+    assert math.isclose(a, b, rel_tol=1e-9, abs_tol=1e-9)
+
+
+def test_append_rows_positions_and_skips():
+    """New rows land at t = L - s_q + i, carry c unchanged and the key rotated to t; a
+    sequence shorter than s_q writes nothing."""
+    rng = np.random.default_rng(6)
+    c = rng.standard_normal((3, 2, 8))
+    kr = rng.standard_normal((3, 2, 4))
+    rows = R.append_rows(c, kr, np.array([10, 1, 64]), 2)
+    assert sorted(rows) == [(0, 8), (0, 9), (2, 62), (2, 63)]
+    assert np.array_equal(rows[(2, 63)][:8], c[2, 1])
+    assert np.allclose(rows[(0, 8)][8:], R.rope_at(kr[0, 0], 8))
+    assert not np.allclose(rows[(0, 8)][8:], kr[0, 0])
