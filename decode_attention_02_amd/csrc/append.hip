@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void append_tokens_kernel(AppendParams a, cons
         const int k = e - a.dc, kk = k % half;
         const int b = n / a.s_q, i = n % a.s_q;
         const double t = static_cast<double>(a.ctx_lens[b] - a.s_q + i);
-        const double ang = t * pow(static_cast<double>(a.rope_theta), -2.0 * kk / a.dr);
+        const double ang = t * a.inv_freq[kk];
         const double cs = cos(ang), sn = sin(ang);
         const double x1 = Elt<T>::load(kr_new, static_cast<int64_t>(n) * a.dr + kk);
         const double x2 = Elt<T>::load(kr_new, static_cast<int64_t>(n) * a.dr + kk + half);
@@ -140,11 +140,132 @@ __global__ __launch_bounds__(256) void append_tokens_kernel(AppendParams a, cons
   }
 }
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// bf16 with d_c % 32 == 0 and (d_n + d_v) % 16 == 0: the projections on MFMA. Workgroup
+// (token tile, group, z) has 4 waves, wave w taking the 16 stacked weight rows
+// 16 * (4z + w) .. +16 of [W_UK^g ; W_UV^g]: K^T/V^T = W C^T with A = 16 weight rows x 32
+// latent values and B = 32 latent values x 16 tokens, both read straight from global
+// memory with every load of the wave in flight at once. The z = 0 workgroups also rotate
+// the tile's keys, write the latent rows (group 0) and copy the keys into K.
+template <int DC>
+__global__ __launch_bounds__(256) void append_tokens_mfma(AppendParams a, const bf16_t* c_new, const bf16_t* kr_new,
+                                                          const bf16_t* w_uk, const bf16_t* w_uv, bf16_t* latent,
+                                                          bf16_t* expanded) {
+  constexpr int KS = DC / 32;
+  const int dq = DC + a.dr;
+  const int dqk = a.dn + a.dr;
+  const int g = blockIdx.y;
+  const int n0 = blockIdx.x * kAppendTile;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  __shared__ int64_t s_dst[kAppendTile];
+  if (threadIdx.x < kAppendTile) {
+    const int n = n0 + threadIdx.x;
+    int64_t dst = -1;
+    if (n < a.n_tok) {
+      const int b = n / a.s_q, i = n % a.s_q;
+      const int L = a.ctx_lens[b];
+      if (L >= a.s_q && L <= a.max_blocks * kBlock) {
+        const int t = L - a.s_q + i;
+        const int32_t id = a.block_table[static_cast<int64_t>(b) * a.max_blocks + t / kBlock];
+        if (id >= 0 && id < a.num_blocks) dst = static_cast<int64_t>(id) * kBlock + t % kBlock;
+      }
+    }
+    s_dst[threadIdx.x] = dst;
+  }
+  const int rows = a.dn + a.dv;
+  const int row0 = 16 * (4 * blockIdx.z + wave);
+  // Issue every operand load of this wave first.
+  const bool live_rows = row0 < rows;
+  bf16x8 wa[KS], cb[KS];
+  if (live_rows) {
+    const int r = row0 + col;
+    const bf16_t* wrow = r < a.dn ? w_uk + (static_cast<int64_t>(g) * a.dn + r) * DC
+                                  : w_uv + (static_cast<int64_t>(g) * a.dv + (r - a.dn)) * DC;
+    const int n = min(n0 + col, a.n_tok - 1);   // past the last token: re-read it, store nothing
+    const bf16_t* crow = c_new + static_cast<int64_t>(n) * DC;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      wa[ks] = *reinterpret_cast<const bf16x8*>(wrow + 32 * ks + 8 * grp);
+      cb[ks] = *reinterpret_cast<const bf16x8*>(crow + 32 * ks + 8 * grp);
+    }
+  }
+  __syncthreads();   // s_dst
+  if (blockIdx.z == 0) {
+    // Rotated keys of the tile (fp64 angle, rounded once), the latent rows, K's RoPE part.
+    __shared__ bf16_t s_rope[kAppendTile * 128];
+    const int half = a.dr / 2;
+    for (int idx = threadIdx.x; idx < kAppendTile * a.dr; idx += blockDim.x) {
+      const int j = idx / a.dr, k = idx % a.dr, kk = k % half;
+      const int n = min(n0 + j, a.n_tok - 1);
+      const int b = n / a.s_q, i = n % a.s_q;
+      const double ang = static_cast<double>(a.ctx_lens[b] - a.s_q + i) * a.inv_freq[kk];
+      const double cs = cos(ang), sn = sin(ang);
+      const double x1 = bf16_to_f32(kr_new[static_cast<int64_t>(n) * a.dr + kk]);
+      const double x2 = bf16_to_f32(kr_new[static_cast<int64_t>(n) * a.dr + kk + half]);
+      s_rope[idx] = f32_to_bf16(static_cast<float>(k < half ? x1 * cs - x2 * sn : x1 * sn + x2 * cs));
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < kAppendTile * a.dr; idx += blockDim.x) {
+      const int j = idx / a.dr, k = idx % a.dr;
+      const int64_t dst = s_dst[j];
+      if (dst < 0) continue;
+      const int64_t id = dst / kBlock;
+      const int s = static_cast<int>(dst % kBlock);
+      const int f = a.dn + k, sl = f / kSlab, w = min(kSlab, dqk - sl * kSlab);
+      bf16_t* chunk = expanded + (id * a.G + g) * static_cast<int64_t>(kBlock) * (dqk + a.dv);
+      chunk[static_cast<int64_t>(sl) * kBlock * kSlab + s * w + f % kSlab] = s_rope[idx];
+      if (g == 0) latent[dst * dq + DC + k] = s_rope[idx];
+    }
+    if (g == 0) {
+      for (int idx = threadIdx.x; idx < kAppendTile * (DC / 8); idx += blockDim.x) {
+        const int j = idx / (DC / 8), c8 = idx % (DC / 8);
+        const int64_t dst = s_dst[j];
+        if (dst < 0) continue;
+        *reinterpret_cast<uint4*>(latent + dst * dq + 8 * c8) =
+            *reinterpret_cast<const uint4*>(c_new + static_cast<int64_t>(n0 + j) * DC + 8 * c8);
+      }
+    }
+  }
+  if (!live_rows) return;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ks], cb[ks], acc, 0, 0, 0);
+  // Lane holds rows row0 + 4*grp + r (r = 0..3) of token col.
+  const int64_t dst = s_dst[col];
+  if (dst < 0) return;
+  const int64_t id = dst / kBlock;
+  const int s = static_cast<int>(dst % kBlock);
+  bf16_t* chunk = expanded + (id * a.G + g) * static_cast<int64_t>(kBlock) * (dqk + a.dv);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = row0 + 4 * grp + r;
+    int64_t off;
+    if (row < a.dn) {
+      const int sl = row / kSlab, w = min(kSlab, dqk - sl * kSlab);
+      off = static_cast<int64_t>(sl) * kBlock * kSlab + s * w + row % kSlab;
+    } else {
+      const int f = row - a.dn;
+      off = static_cast<int64_t>(kBlock) * dqk + (s / kHalf) * a.dv * kHalf + f * kHalf + s % kHalf;
+    }
+    chunk[off] = f32_to_bf16(acc[r]);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_append(const AppendParams& a, const void* c_new, const void* kr_new, const void* w_uk,
                          const void* w_uv, void* latent, void* expanded, bool bf16, hipStream_t s) {
   const int tiles = (a.n_tok + kAppendTile - 1) / kAppendTile;
+  if (bf16 && expanded != nullptr && a.dc == 512 && a.dr <= 128 && (a.dn + a.dv) % 16 == 0) {
+    dim3 grid(tiles, a.G, (a.dn + a.dv + 63) / 64);
+    append_tokens_mfma<512><<<grid, 256, 0, s>>>(a, static_cast<const bf16_t*>(c_new), static_cast<const bf16_t*>(kr_new),
+                                                 static_cast<const bf16_t*>(w_uk), static_cast<const bf16_t*>(w_uv),
+                                                 static_cast<bf16_t*>(latent), static_cast<bf16_t*>(expanded));
+    return hipGetLastError();
+  }
   dim3 grid(tiles, expanded != nullptr ? a.G : 1);
   const size_t lds = sizeof(float) * kAppendTile * (a.dc + a.dr);
   if (bf16) {

@@ -388,6 +388,7 @@ gqla_status gqla_append_tokens(const gqla_dims* dims, const gqla_paged* paged, c
   if (!(rope_theta > 0.f)) return fail(GQLA_ERR_INVALID_ARG, "rope_theta must be > 0");
   if (dims->rope_dim % 2 != 0) return fail(GQLA_ERR_INVALID_ARG, "rope_dim must be even (rotation pairs)");
   if (dims->latent_rank % 8 != 0) return fail(GQLA_ERR_UNSUPPORTED, "append needs latent_rank % 8 == 0");
+  if (dims->rope_dim > 128) return fail(GQLA_ERR_UNSUPPORTED, "append supports rope_dim <= 128");
   if (static_cast<int64_t>(16) * (dims->latent_rank + dims->rope_dim) * 4 > 160 * 1024)
     return fail(GQLA_ERR_UNSUPPORTED, "latent row too wide for the append kernel's LDS tile");
   const int64_t n_tok = static_cast<int64_t>(dims->batch) * dims->s_q;
@@ -405,6 +406,8 @@ gqla_status gqla_append_tokens(const gqla_dims* dims, const gqla_paged* paged, c
   a.dn = dims->nope_dim;
   a.dv = dims->v_dim;
   a.rope_theta = rope_theta;
+  for (int k = 0; k < dims->rope_dim / 2; ++k)
+    a.inv_freq[k] = std::pow(static_cast<double>(rope_theta), -2.0 * k / dims->rope_dim);
   hipError_t e = gqla::launch_append(a, c_new, kr_new, w_uk, w_uv, latent_cache, expanded_cache,
                                      dims->dtype == GQLA_BF16, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GQLA_OK : hip_fail(e, "append launch");

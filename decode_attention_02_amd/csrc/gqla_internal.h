@@ -77,6 +77,7 @@ struct AppendParams {
   int32_t n_tok, s_q, G;
   int32_t dc, dr, dn, dv;
   float rope_theta;
+  double inv_freq[64];   // rope_theta^(-2k/d_R), k < d_R / 2 (fp64, from the host)
 };
 hipError_t launch_append(const AppendParams& a, const void* c_new, const void* kr_new, const void* w_uk,
                          const void* w_uv, void* latent, void* expanded, bool bf16, hipStream_t s);
