@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--absorb-sq", type=int, default=1)
     ap.add_argument("--gqa-sq", type=int, default=2)
+    ap.add_argument("--gqa-layout", choices=("shared-rope", "per-group"), default="shared-rope",
+                    help="expanded cache: RoPE key once per block (default) or in every group's K")
     ap.add_argument("--profile", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     return ap.parse_args()
@@ -54,7 +56,7 @@ def source_sha(path=DOMINANT_SRC):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()
 
 
-def summarize_pmc(fetch_dir, write_dir, workload_name):
+def summarize_pmc(fetch_dir, write_dir, workload_name, layout):
     """Per-dispatch HBM traffic of the GQA decode kernel from FETCH_SIZE / WRITE_SIZE
     passes, each scaled by what the counter reads for the 1 GiB calibration copy."""
     def per_kernel(d, counter):
@@ -79,7 +81,7 @@ def summarize_pmc(fetch_dir, write_dir, workload_name):
     w_scale = CALIB_BYTES / max(wr.get(big, [0.0]))     # and writes CALIB_BYTES
     fetch = float(np.mean(f[gqa[0]])) * f_scale
     write = float(np.mean(wr[gqa[0]])) * w_scale
-    return {"workload": workload_name, "kernel": gqa[0], "source_sha256": source_sha(),
+    return {"workload": workload_name, "gqa_expanded_layout": layout, "kernel": gqa[0], "source_sha256": source_sha(),
             "fetch_bytes": fetch, "write_bytes": write, "traffic_bytes": fetch + write,
             "raw_fetch_bytes": float(np.mean(f[gqa[0]])), "raw_write_bytes": float(np.mean(wr[gqa[0]])),
             "calibration": {"copy_kernel": big, "bytes": CALIB_BYTES, "fetch_scale": f_scale, "write_scale": w_scale},
@@ -88,13 +90,15 @@ def summarize_pmc(fetch_dir, write_dir, workload_name):
                          "python bench.py --summarize-pmc <FETCH_DIR> <WRITE_DIR>"]}
 
 
-def load_traffic(workload_name):
-    """Measured traffic of the current GQA decode source on this workload, else None."""
+def load_traffic(workload_name, layout):
+    """Measured traffic of the current GQA decode source on this workload and expanded-cache
+    layout, else None."""
     try:
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256") != source_sha() or t.get("workload") != workload_name:
+    if (t.get("source_sha256") != source_sha() or t.get("workload") != workload_name
+            or t.get("gqa_expanded_layout") != layout):
         return None
     return t["traffic_bytes"]
 
@@ -139,7 +143,7 @@ def cpu_baseline(x, q_abs_sq, gqa_sq, budget_s):
 def main():
     a = parse()
     if a.summarize_pmc:
-        print(json.dumps(summarize_pmc(*a.summarize_pmc, a.workload), indent=1))
+        print(json.dumps(summarize_pmc(*a.summarize_pmc, a.workload, a.gqa_layout), indent=1))
         return
     if a.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {a.gpus} is not supported (this build has no "
@@ -171,7 +175,7 @@ def main():
     mk = dict(batch=B, num_heads=H, num_groups=w.groups, latent_rank=w.latent, rope_dim=w.rope,
               nope_dim=w.nope, v_dim=w.v, dtype=G.GQLA_BF16)
     d_abs = G.Dims(s_q=a.absorb_sq, **mk)
-    d_gqa = G.Dims(s_q=a.gqa_sq, **mk)
+    d_gqa = G.Dims(s_q=a.gqa_sq, rope_shared=int(a.gqa_layout == "shared-rope"), **mk)
 
     def workspace(d, path):
         n = G.gqla_workspace_bytes(d, path, table.shape[1], max_ctx, x.num_blocks)
@@ -180,7 +184,7 @@ def main():
     ws_abs, ws_gqa = workspace(d_abs, G.GQLA_PATH_ABSORB), workspace(d_gqa, G.GQLA_PATH_GQA)
     splits = {"absorb": G.gqla_num_splits(d_abs, 0, table.shape[1], max_ctx, x.num_blocks),
               "gqa": G.gqla_num_splits(d_gqa, 1, table.shape[1], max_ctx, x.num_blocks)}
-    per_block = w.groups * 64 * (w.qk + w.v)
+    per_block = 64 * G.gqla_cache_bytes_per_token(d_gqa, G.GQLA_PATH_GQA) // 2   # bf16 values per block
     expanded = torch.empty(x.num_blocks * per_block, dtype=torch.bfloat16, device="cuda")
     all_ids = torch.arange(x.num_blocks, dtype=torch.int32, device="cuda")
     G.gqla_expand_cache(d_gqa, cache, w_uk, w_uv, all_ids, x.num_blocks, expanded)
@@ -260,7 +264,7 @@ def main():
     ctx = x.ctx_lens.astype(np.int64)
     elt = 2
     kv_abs = float(ctx.sum() * (w.latent + w.rope) * elt)
-    kv_gqa = float(ctx.sum() * w.groups * (w.qk + w.v) * elt)
+    kv_gqa = float(ctx.sum() * G.gqla_cache_bytes_per_token(d_gqa, G.GQLA_PATH_GQA))
     vis = lambda s_q: float(sum(sum(L - s_q + 1 + i for i in range(s_q)) for L in ctx))  # noqa: E731
     fl_abs = vis(a.absorb_sq) * H * 2 * (2 * w.latent + w.rope)
     fl_gqa = vis(a.gqa_sq) * H * 2 * (w.qk + w.v)
@@ -275,6 +279,7 @@ def main():
         "config": {"workload": w.name, "batch": B, "context": int(ctx.max()), "heads": H,
                    "groups": w.groups, "latent": w.latent, "rope": w.rope, "nope": w.nope, "v": w.v,
                    "s_q": {"absorb": a.absorb_sq, "gqa": a.gqa_sq},
+                   "gqa_expanded_layout": a.gqa_layout,
                    "block_table": "shuffled" if w.shuffled else "identity", "block_size": 64,
                    "splits": splits},
         "paths": {
@@ -291,7 +296,7 @@ def main():
         },
         "roofline": {"kernel": "gqa_decode_split (gqla_decode_gqa)", "bound": "hbm",
                      "achieved": kv_gqa / (t_gqa / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": kv_gqa / (t_gqa / 1e3) / 1e9 / HBM_PEAK_GBS, "traffic": load_traffic(w.name),
+                     "frac": kv_gqa / (t_gqa / 1e3) / 1e9 / HBM_PEAK_GBS, "traffic": load_traffic(w.name, a.gqa_layout),
                      "algorithmic_bytes_per_launch": kv_gqa, "avg_launch_ms": t_gqa},
     }
     if not a.no_cpu_baseline:

@@ -36,7 +36,7 @@ class gqla_dims(ctypes.Structure):
                 ("rope_dim", ctypes.c_int32), ("nope_dim", ctypes.c_int32),
                 ("v_dim", ctypes.c_int32), ("s_q", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float)]
+                ("softmax_scale", ctypes.c_float), ("rope_shared", ctypes.c_int32)]
 
 
 class gqla_paged(ctypes.Structure):
@@ -100,11 +100,12 @@ class Dims:
     dtype: int = GQLA_BF16
     block_size: int = 64
     softmax_scale: float = 0.0
+    rope_shared: int = 0
 
     def c(self) -> gqla_dims:
         return gqla_dims(self.batch, self.num_heads, self.num_groups, self.latent_rank,
                          self.rope_dim, self.nope_dim, self.v_dim, self.s_q, self.block_size,
-                         self.dtype, self.softmax_scale)
+                         self.dtype, self.softmax_scale, self.rope_shared)
 
 
 @dataclass

@@ -43,9 +43,9 @@ __global__ __launch_bounds__(256) void append_tokens_kernel(AppendParams a, cons
                                                             const T* w_uk, const T* w_uv, T* latent, T* expanded) {
   extern __shared__ __attribute__((aligned(16))) float s_row[];   // [kAppendTile][d_c + d_R]
   const int dq = a.dc + a.dr;
-  const int dqk = a.dn + a.dr;
   const int g = blockIdx.y;
   const int n0 = blockIdx.x * kAppendTile;
+  const ExpandedLayout lay = expanded_layout(a.dn, a.dr, a.dv, a.G, a.rope_shared != 0);
   __shared__ int64_t s_dst[kAppendTile];   // latent row index (block * 64 + slot), -1 = skip
   if (threadIdx.x < kAppendTile) {
     const int n = n0 + threadIdx.x;
@@ -118,24 +118,29 @@ __global__ __launch_bounds__(256) void append_tokens_kernel(AppendParams a, cons
       for (int j = 0; j < kAppendTile; ++j) acc[j] = s_row[j * dq + a.dc + (r - rows)];
     }
     // Key feature f (nope rows, then RoPE) or value feature of slot s, in the expanded
-    // chunk's slab layout (see gqla_expand_cache).
+    // cache's slab layout (see gqla_expand_cache); a shared RoPE key goes to the block's
+    // key area, written by group 0 only.
     const bool is_v = r >= a.dn && r < rows;
     const int f = r < a.dn ? r : (is_v ? r - a.dn : a.dn + (r - rows));
+    const bool shared_key = !is_v && f >= lay.k_feats;
+    if (shared_key && g != 0) continue;
 #pragma unroll
     for (int j = 0; j < kAppendTile; ++j) {
       const int64_t dst = s_dst[j];
       if (dst < 0) continue;
       const int64_t id = dst / kBlock;
       const int s = static_cast<int>(dst % kBlock);
-      T* chunk = expanded + (id * a.G + g) * static_cast<int64_t>(kBlock) * (dqk + a.dv);
-      int64_t off;
+      T* blk = expanded + id * lay.block;
+      T* chunk = blk + lay.rope + g * lay.chunk;
       if (is_v) {
-        off = static_cast<int64_t>(kBlock) * dqk + (s / kHalf) * a.dv * kHalf + f * kHalf + s % kHalf;
+        Elt<T>::store(chunk, static_cast<int64_t>(kBlock) * lay.k_feats + (s / kHalf) * a.dv * kHalf + f * kHalf + s % kHalf, acc[j]);
+      } else if (!shared_key) {
+        const int sl = f / kSlab, w = min(kSlab, lay.k_feats - sl * kSlab);
+        Elt<T>::store(chunk, static_cast<int64_t>(sl) * kBlock * kSlab + s * w + f % kSlab, acc[j]);
       } else {
-        const int sl = f / kSlab, w = min(kSlab, dqk - sl * kSlab);
-        off = static_cast<int64_t>(sl) * kBlock * kSlab + s * w + f % kSlab;
+        const int fr = f - a.dn, sl = fr / kSlab, w = min(kSlab, a.dr - sl * kSlab);
+        Elt<T>::store(blk, static_cast<int64_t>(sl) * kBlock * kSlab + s * w + fr % kSlab, acc[j]);
       }
-      Elt<T>::store(chunk, off, acc[j]);
     }
   }
 }
@@ -155,7 +160,7 @@ __global__ __launch_bounds__(256) void append_tokens_mfma(AppendParams a, const 
                                                           bf16_t* expanded) {
   constexpr int KS = DC / 32;
   const int dq = DC + a.dr;
-  const int dqk = a.dn + a.dr;
+  const ExpandedLayout lay = expanded_layout(a.dn, a.dr, a.dv, a.G, a.rope_shared != 0);
   const int g = blockIdx.y;
   const int n0 = blockIdx.x * kAppendTile;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -214,9 +219,14 @@ __global__ __launch_bounds__(256) void append_tokens_mfma(AppendParams a, const 
       if (dst < 0) continue;
       const int64_t id = dst / kBlock;
       const int s = static_cast<int>(dst % kBlock);
-      const int f = a.dn + k, sl = f / kSlab, w = min(kSlab, dqk - sl * kSlab);
-      bf16_t* chunk = expanded + (id * a.G + g) * static_cast<int64_t>(kBlock) * (dqk + a.dv);
-      chunk[static_cast<int64_t>(sl) * kBlock * kSlab + s * w + f % kSlab] = s_rope[idx];
+      bf16_t* blk = expanded + id * lay.block;
+      if (!a.rope_shared) {   // into this group's K
+        const int f = a.dn + k, sl = f / kSlab, w = min(kSlab, lay.k_feats - sl * kSlab);
+        blk[lay.rope + g * lay.chunk + static_cast<int64_t>(sl) * kBlock * kSlab + s * w + f % kSlab] = s_rope[idx];
+      } else if (g == 0) {    // once, into the block's shared key area
+        const int sl = k / kSlab, w = min(kSlab, a.dr - sl * kSlab);
+        blk[static_cast<int64_t>(sl) * kBlock * kSlab + s * w + k % kSlab] = s_rope[idx];
+      }
       if (g == 0) latent[dst * dq + DC + k] = s_rope[idx];
     }
     if (g == 0) {
@@ -238,17 +248,17 @@ __global__ __launch_bounds__(256) void append_tokens_mfma(AppendParams a, const 
   if (dst < 0) return;
   const int64_t id = dst / kBlock;
   const int s = static_cast<int>(dst % kBlock);
-  bf16_t* chunk = expanded + (id * a.G + g) * static_cast<int64_t>(kBlock) * (dqk + a.dv);
+  bf16_t* chunk = expanded + id * lay.block + lay.rope + g * lay.chunk;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int row = row0 + 4 * grp + r;
     int64_t off;
     if (row < a.dn) {
-      const int sl = row / kSlab, w = min(kSlab, dqk - sl * kSlab);
+      const int sl = row / kSlab, w = min(kSlab, lay.k_feats - sl * kSlab);
       off = static_cast<int64_t>(sl) * kBlock * kSlab + s * w + row % kSlab;
     } else {
       const int f = row - a.dn;
-      off = static_cast<int64_t>(kBlock) * dqk + (s / kHalf) * a.dv * kHalf + f * kHalf + s % kHalf;
+      off = static_cast<int64_t>(kBlock) * lay.k_feats + (s / kHalf) * a.dv * kHalf + f * kHalf + s % kHalf;
     }
     chunk[off] = f32_to_bf16(acc[r]);
   }

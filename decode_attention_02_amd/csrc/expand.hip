@@ -83,6 +83,8 @@ struct ExpandCta {
   int g, j0, nj;
   int lane, wave, col, grp;
   bool is_key;
+  ExpandedLayout lay;   // this cache's block layout (RoPE key per group or shared)
+  int k_feats;          // K features stored in each group chunk
   int row0;                 // first weight row of this wave within its matrix
   bf16x8 wf[2][KS];         // the wave's weight rows, MFMA operand layout
   int base_even, base_odd;  // per-lane LDS offsets of the latent operand
@@ -147,7 +149,7 @@ struct ExpandCta {
           // inside the 32-token half tok / 32
           const int f = row0 + 16 * ft + col;
           const int tok = tt * 16 + 4 * grp;
-          *reinterpret_cast<uint2*>(chunk + kBlock * DQK + (tok / kHalf) * kDV * kHalf + f * kHalf + tok % kHalf) =
+          *reinterpret_cast<uint2*>(chunk + kBlock * k_feats + (tok / kHalf) * kDV * kHalf + f * kHalf + tok % kHalf) =
               *reinterpret_cast<uint2*>(packed);
         }
       }
@@ -157,15 +159,20 @@ struct ExpandCta {
   template <int BUF>
   __device__ __forceinline__ void compute(int id) {
     const char* tile = etile<BUF>();
-    bf16_t* chunk = expanded + (static_cast<int64_t>(id) * d.G + g) * kBlock * (DQK + kDV);
+    bf16_t* blk = expanded + static_cast<int64_t>(id) * lay.block;
+    bf16_t* chunk = blk + lay.rope + g * lay.chunk;
     if (is_key) tiles<BUF, true>(chunk);
     else tiles<BUF, false>(chunk);
-    // RoPE key copy: 64 tokens x 64 values, 16 bytes per lane-step over the workgroup.
+    // RoPE key copy: 64 tokens x 64 values, 16 bytes per lane-step over the workgroup; into
+    // every group's K, or once per block into the shared key area.
+    if (d.rope_shared && g != 0) return;
+    bf16_t* kdst = d.rope_shared ? blk : chunk;
+    const int kf0 = d.rope_shared ? 0 : DN;
     for (int i = threadIdx.x; i < kBlock * kDR / 8; i += W * 64) {
       const int tok = i / (kDR / 8), c = kDC / 8 + i % (kDR / 8);
       const uint4 v = *reinterpret_cast<const uint4*>(tile + tok * kRowBytes + (((c & ~7) | ((c & 7) ^ swz(tok))) << 4));
-      const int f = DN + 8 * (i % (kDR / 8));
-      *reinterpret_cast<uint4*>(chunk + (f / kSlab) * kBlock * kSlab + tok * kSlab + f % kSlab) = v;
+      const int fk = kf0 + 8 * (i % (kDR / 8));
+      *reinterpret_cast<uint4*>(kdst + (fk / kSlab) * kBlock * kSlab + tok * kSlab + fk % kSlab) = v;
     }
   }
 
@@ -190,6 +197,8 @@ struct ExpandCta {
     wave = threadIdx.x >> 6;
     col = lane & 15;
     grp = lane >> 4;
+    lay = expanded_layout(DN, kDR, kDV, d.G, d.rope_shared != 0);
+    k_feats = lay.k_feats;
     is_key = wave * 32 < DN;
     row0 = is_key ? wave * 32 : wave * 32 - DN;
     const bf16_t* wmat = is_key ? w_uk + static_cast<int64_t>(g) * DN * kDC : w_uv + static_cast<int64_t>(g) * kDV * kDC;

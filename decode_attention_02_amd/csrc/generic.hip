@@ -18,14 +18,19 @@ size_t generic_attn_lds_bytes(int dk, int dvo) {
   return sizeof(float) * (static_cast<size_t>(kGenRows) * (dk + kBlock + dvo) + 3 * kGenRows);
 }
 
-// Offset of key feature f of slot t inside a kv head's block: plain strides for the
-// latent, or the expanded cache's slabs (features [32s, 32s + w_s) of all 64 slots stored
-// slot-major, w_s = min(32, dk - 32s)).
-__device__ __forceinline__ int64_t kv_k_index(const AttnParams& p, int t, int f) {
-  if (p.k_slab == 0) return static_cast<int64_t>(t) * p.k_ts + static_cast<int64_t>(f) * p.k_fs;
-  const int s = f / p.k_slab;
-  const int w = min(p.k_slab, p.dk - s * p.k_slab);
-  return static_cast<int64_t>(s) * kBlock * p.k_slab + t * w + (f - s * p.k_slab);
+// Key feature f of slot t: plain strides for the latent, or the expanded cache's slabs
+// (features [32s, 32s + w_s) of all 64 slots stored slot-major, w_s the slab's width),
+// features [0, k_own) in the group chunk at `base`, the rest (a shared RoPE key) in the
+// block's key area at `rbase`.
+template <typename T>
+__device__ __forceinline__ float kv_k_load(const AttnParams& p, const T* base, const T* rbase, int t, int f) {
+  if (p.k_slab == 0) return Elt<T>::load(base, static_cast<int64_t>(t) * p.k_ts + static_cast<int64_t>(f) * p.k_fs);
+  const bool own = f < p.k_own;
+  const int ff = own ? f : f - p.k_own;
+  const int nf = own ? p.k_own : p.dk - p.k_own;
+  const int s = ff / p.k_slab;
+  const int w = min(p.k_slab, nf - s * p.k_slab);
+  return Elt<T>::load(own ? base : rbase, static_cast<int64_t>(s) * kBlock * p.k_slab + t * w + (ff - s * p.k_slab));
 }
 
 __device__ __forceinline__ int64_t kv_v_index(const AttnParams& p, int t, int f) {
@@ -76,7 +81,8 @@ __global__ __launch_bounds__(kGenThreads) void generic_attn_split(AttnParams p) 
   for (int blk = blk_lo; blk < blk_hi; ++blk) {
     const int32_t id = p.block_table[static_cast<int64_t>(b) * p.max_blocks + blk];
     if (id < 0 || id >= p.num_blocks) { bad = true; break; }   // uniform across the group
-    const T* base = kv + static_cast<int64_t>(id) * p.block_stride + kvh * p.kvh_stride;
+    const T* rbase = kv + static_cast<int64_t>(id) * p.block_stride;
+    const T* base = rbase + p.kv_off + kvh * p.kvh_stride;
     for (int idx = tid; idx < nr * kBlock; idx += kGenThreads) {
       const int r = idx / kBlock, t = idx % kBlock, rr = r0 + r;
       const int n = L - p.s_q + 1 + rr / p.heads_per_kv;
@@ -84,7 +90,7 @@ __global__ __launch_bounds__(kGenThreads) void generic_attn_split(AttnParams p) 
       if (blk * kBlock + t < n) {
         float acc = 0.f;
         for (int f = 0; f < p.dk; ++f)
-          acc += sq[r * p.dk + f] * Elt<T>::load(base, kv_k_index(p, t, f));
+          acc += sq[r * p.dk + f] * kv_k_load(p, base, rbase, t, f);
         s = acc * p.scale;
       }
       ss[idx] = s;
@@ -266,9 +272,9 @@ hipError_t launch_generic_out_proj(const ProjParams& d, const float* o_lat, cons
   return hipGetLastError();
 }
 
-// Expanded chunk of (block id, group g): K in slabs of 32 features ([64][w_s] each, the
-// last one narrower when d_qk is not a multiple of 32), then V as two 32-slot halves
-// [d_v][32].
+// Expanded block of id: an optional shared RoPE key area, then per group K in slabs of 32
+// features ([64][w_s] each, the last narrower when the feature count is not a multiple of
+// 32), then V as two 32-slot halves [d_v][32].
 template <typename T>
 __global__ __launch_bounds__(256) void generic_expand(ProjParams d, const T* latent, const T* w_uk, const T* w_uv,
                                                       const int32_t* block_ids, int64_t num_blocks, T* expanded) {
@@ -276,8 +282,10 @@ __global__ __launch_bounds__(256) void generic_expand(ProjParams d, const T* lat
   if (id < 0 || id >= num_blocks) return;
   const int g = blockIdx.y;
   const int dq = d.dc + d.dr, dqk = d.dn + d.dr;
+  const ExpandedLayout lay = expanded_layout(d.dn, d.dr, d.dv, d.G, d.rope_shared != 0);
   const T* src = latent + static_cast<int64_t>(id) * kBlock * dq;
-  T* dst = expanded + (static_cast<int64_t>(id) * d.G + g) * kBlock * (dqk + d.dv);
+  T* blk = expanded + static_cast<int64_t>(id) * lay.block;
+  T* dst = blk + lay.rope + g * lay.chunk;
   for (int idx = threadIdx.x; idx < kBlock * dqk; idx += blockDim.x) {
     const int r = idx / dqk, e = idx % dqk;
     float acc;
@@ -288,15 +296,20 @@ __global__ __launch_bounds__(256) void generic_expand(ProjParams d, const T* lat
     } else {
       acc = Elt<T>::load(src, static_cast<int64_t>(r) * dq + d.dc + (e - d.dn));
     }
-    const int s = e / kSlab, w = min(kSlab, dqk - s * kSlab);
-    Elt<T>::store(dst, static_cast<int64_t>(s) * kBlock * kSlab + r * w + (e - s * kSlab), acc);
+    if (e < lay.k_feats) {
+      const int s = e / kSlab, w = min(kSlab, lay.k_feats - s * kSlab);
+      Elt<T>::store(dst, static_cast<int64_t>(s) * kBlock * kSlab + r * w + (e - s * kSlab), acc);
+    } else if (g == 0) {   // shared RoPE key, written once per block
+      const int f = e - d.dn, s = f / kSlab, w = min(kSlab, d.dr - s * kSlab);
+      Elt<T>::store(blk, static_cast<int64_t>(s) * kBlock * kSlab + r * w + (f - s * kSlab), acc);
+    }
   }
   for (int idx = threadIdx.x; idx < d.dv * kBlock; idx += blockDim.x) {
     const int f = idx / kBlock, r = idx % kBlock;
     float acc = 0.f;
     for (int c = 0; c < d.dc; ++c)
       acc += Elt<T>::load(src, static_cast<int64_t>(r) * dq + c) * Elt<T>::load(w_uv, (static_cast<int64_t>(g) * d.dv + f) * d.dc + c);
-    Elt<T>::store(dst, static_cast<int64_t>(kBlock) * dqk + (r / kHalf) * d.dv * kHalf + f * kHalf + r % kHalf, acc);
+    Elt<T>::store(dst, static_cast<int64_t>(kBlock) * lay.k_feats + (r / kHalf) * d.dv * kHalf + f * kHalf + r % kHalf, acc);
   }
 }
 

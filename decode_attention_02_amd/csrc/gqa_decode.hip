@@ -58,12 +58,16 @@ __device__ __forceinline__ float xor_sum(float v) {
 }
 
 // RT = 16-row MFMA column tiles of query rows per group (gs * s_q <= 16 * RT); with two,
-// every K and V operand load feeds both tiles.
-template <int DQK, int DV, int kWaves, int RT>
+// every K and V operand load feeds both tiles. SHARED: the expanded cache keeps the RoPE
+// key (d_R = 64) once per block; its K slabs come from the block's key area, and the
+// workgroups of one sequence's groups are placed on one XCD so that area is fetched from
+// HBM once and served to the other groups from that XCD's L2.
+template <int DQK, int DV, int kWaves, int RT, bool SHARED>
 __global__ __launch_bounds__(kWaves * 64) void gqa_decode_split(AttnParams p) {
   constexpr int KS = DQK / 32;     // k-steps of the score product
+  constexpr int KSN = SHARED ? (DQK - 64) / 32 : KS;   // k-steps held in the group chunk
+  constexpr int KF = 32 * KSN;     // K features in the group chunk
   constexpr int NT = DV / 16;      // feature tiles of the value product
-  constexpr int CHUNK = kBlock * (DQK + DV);
   constexpr bool kHalfUnits = RT == 2 && DQK > 128;
   __shared__ float s_o[kWaves][RT][NT][64][4];   // per-wave O^T fragments (lane-major)
   __shared__ float s_m[kWaves][RT * 16];
@@ -74,10 +78,22 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_split(AttnParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15;          // query row owned by this lane in each tile (MFMA column)
   const int grp = lane >> 4;          // k-group of the MFMA operands
-  const int split = blockIdx.x % p.n_split;
-  const int bg = blockIdx.x / p.n_split;
-  const int g = bg % p.kv_heads;
-  const int b = bg / p.kv_heads;
+  int split, g, b;
+  if constexpr (SHARED) {
+    // id = ((u / 8) * G + g) * 8 + u % 8 for unit u = (sequence, split): a unit's groups
+    // share an XCD (ids equal mod 8) and are dispatched together.
+    const int x = blockIdx.x & 7, y = blockIdx.x >> 3;
+    g = y % p.kv_heads;
+    const int u = (y / p.kv_heads) * 8 + x;
+    if (u >= p.B * p.n_split) return;
+    split = u % p.n_split;
+    b = u / p.n_split;
+  } else {
+    split = blockIdx.x % p.n_split;
+    const int bg = blockIdx.x / p.n_split;
+    g = bg % p.kv_heads;
+    b = bg / p.kv_heads;
+  }
   const int gs = p.heads_per_kv;
   const int rows = gs * p.s_q;
 
@@ -140,7 +156,7 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_split(AttnParams p) {
     return __builtin_amdgcn_readlane(ids, j & 63);
   };
   auto chunk_of = [&](int id) -> const bf16_t* {
-    return kv + (static_cast<int64_t>(id) * p.kv_heads + g) * CHUNK;
+    return kv + static_cast<int64_t>(id) * p.block_stride + p.kv_off + g * p.kvh_stride;
   };
 
   // One half block's operands: K rows of its 32 tokens, permuted so lane group `grp`
@@ -153,13 +169,16 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_split(AttnParams p) {
     bf16x8 v[NT];
   };
   auto load_half = [&](Half& f, const bf16_t* chunk, int half) {
-    const bf16_t* vt = chunk + kBlock * DQK;
+    const bf16_t* vt = chunk + kBlock * KF;
+    const bf16_t* rk = chunk - (p.kv_off + g * p.kvh_stride);   // the block's shared key area
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const int tok = 32 * half + 8 * (col >> 2) + 4 * tt + (col & 3);
       const bf16_t* krow = chunk + tok * kSlab + 8 * grp;
+      const bf16_t* rrow = rk + tok * kSlab + 8 * grp;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) f.k[tt][ks] = load8_stream(krow + ks * kBlock * kSlab);
+      for (int ks = 0; ks < KS; ++ks)
+        f.k[tt][ks] = load8_stream(ks < KSN ? krow + ks * kBlock * kSlab : rrow + (ks - KSN) * kBlock * kSlab);
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
@@ -336,7 +355,8 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_split(AttnParams p) {
 bool tuned_gqa_supported(const gqla_dims* d) {
   const int dqk = d->nope_dim + d->rope_dim;
   const int gs = d->num_heads / d->num_groups;
-  return d->dtype == GQLA_BF16 && (dqk == 128 || dqk == 192) && d->v_dim == 128 && gs * d->s_q <= 32;
+  return d->dtype == GQLA_BF16 && (dqk == 128 || dqk == 192) && d->v_dim == 128 && gs * d->s_q <= 32 &&
+         (d->rope_shared == 0 || d->rope_dim == 64);
 }
 
 // One 4-wave workgroup per CU per round: on MI355X the unsplit launch streams fastest
@@ -345,19 +365,25 @@ bool tuned_gqa_supported(const gqla_dims* d) {
 int tuned_gqa_target_wgs() { return kNumCUs; }
 int tuned_gqa_min_blocks_per_split() { return 8; }
 
-template <int DQK, int RT>
-hipError_t launch_dqk(const AttnParams& p, int64_t wgs, hipStream_t s) {
+template <int DQK, int RT, bool SHARED>
+hipError_t launch_dqk(const AttnParams& p, hipStream_t s) {
   constexpr int kWaves = 4;
-  gqa_decode_split<DQK, 128, kWaves, RT><<<static_cast<unsigned>(wgs), kWaves * 64, 0, s>>>(p);
+  const int64_t units = static_cast<int64_t>(p.B) * p.n_split;
+  const int64_t wgs = SHARED ? (units + 7) / 8 * 8 * p.kv_heads : units * p.kv_heads;
+  if (wgs > 0x7fffffff) return hipErrorInvalidConfiguration;
+  gqa_decode_split<DQK, 128, kWaves, RT, SHARED><<<static_cast<unsigned>(wgs), kWaves * 64, 0, s>>>(p);
   return hipGetLastError();
 }
 
-hipError_t launch_tuned_gqa(const AttnParams& p, const gqla_dims* d, hipStream_t s) {
-  const int64_t wgs = static_cast<int64_t>(p.B) * p.kv_heads * p.n_split;
-  if (wgs > 0x7fffffff) return hipErrorInvalidConfiguration;
+template <bool SHARED>
+hipError_t launch_layout(const AttnParams& p, const gqla_dims* d, hipStream_t s) {
   const bool two = p.heads_per_kv * p.s_q > 16;
-  if (d->nope_dim + d->rope_dim == 192) return two ? launch_dqk<192, 2>(p, wgs, s) : launch_dqk<192, 1>(p, wgs, s);
-  return two ? launch_dqk<128, 2>(p, wgs, s) : launch_dqk<128, 1>(p, wgs, s);
+  if (d->nope_dim + d->rope_dim == 192) return two ? launch_dqk<192, 2, SHARED>(p, s) : launch_dqk<192, 1, SHARED>(p, s);
+  return two ? launch_dqk<128, 2, SHARED>(p, s) : launch_dqk<128, 1, SHARED>(p, s);
+}
+
+hipError_t launch_tuned_gqa(const AttnParams& p, const gqla_dims* d, hipStream_t s) {
+  return d->rope_shared ? launch_layout<true>(p, d, s) : launch_layout<false>(p, d, s);
 }
 
 }  // namespace gqla

@@ -43,6 +43,8 @@ gqla_status check_dims(const gqla_dims* d) {
     return fail(GQLA_ERR_INVALID_ARG, "block_size must be 64 (got %d)", d->block_size);
   if (d->dtype != GQLA_F32 && d->dtype != GQLA_BF16)
     return fail(GQLA_ERR_INVALID_ARG, "unknown dtype %d", d->dtype);
+  if (d->rope_shared != 0 && d->rope_shared != 1)
+    return fail(GQLA_ERR_INVALID_ARG, "rope_shared must be 0 or 1 (got %d)", d->rope_shared);
   return GQLA_OK;
 }
 
@@ -145,12 +147,16 @@ gqla_status run_decode(const gqla_dims* d, const gqla_paged* pg, int32_t path, c
     a.heads_per_kv = d->num_heads / d->num_groups;
     a.dk = dqk;
     a.dvo = d->v_dim;
-    a.kvh_stride = static_cast<int64_t>(gqla::kBlock) * (dqk + d->v_dim);
-    a.block_stride = a.kvh_stride * d->num_groups;
+    const gqla::ExpandedLayout lay =
+        gqla::expanded_layout(d->nope_dim, d->rope_dim, d->v_dim, d->num_groups, d->rope_shared != 0);
+    a.kvh_stride = lay.chunk;
+    a.block_stride = lay.block;
+    a.kv_off = lay.rope;
+    a.k_own = lay.k_feats;
     a.k_ts = 0;
     a.k_fs = 0;
     a.k_slab = gqla::kSlab;
-    a.v_off = gqla::kBlock * dqk;
+    a.v_off = gqla::kBlock * lay.k_feats;
     a.v_half = gqla::kHalf * d->v_dim;
     a.v_ts = 1;
     a.v_fs = gqla::kHalf;
@@ -162,6 +168,8 @@ gqla_status run_decode(const gqla_dims* d, const gqla_paged* pg, int32_t path, c
     a.dvo = d->latent_rank;
     a.kvh_stride = 0;
     a.block_stride = static_cast<int64_t>(gqla::kBlock) * dq;
+    a.kv_off = 0;
+    a.k_own = dq;
     a.k_ts = dq;
     a.k_fs = 1;
     a.k_slab = 0;
@@ -205,6 +213,7 @@ gqla::ProjParams proj_params(const gqla_dims* d) {
   p.dr = d->rope_dim;
   p.dn = d->nope_dim;
   p.dv = d->v_dim;
+  p.rope_shared = d->rope_shared;
   return p;
 }
 
@@ -308,7 +317,8 @@ int64_t gqla_cache_bytes_per_token(const gqla_dims* dims, int32_t path) {
   if (check_dims(dims) != GQLA_OK || check_path(path) != GQLA_OK) return 0;
   const int64_t elt = elt_bytes(dims);
   if (path == GQLA_PATH_ABSORB) return (dims->latent_rank + dims->rope_dim) * elt;
-  return static_cast<int64_t>(dims->num_groups) * (dims->nope_dim + dims->rope_dim + dims->v_dim) * elt;
+  return gqla::expanded_layout(dims->nope_dim, dims->rope_dim, dims->v_dim, dims->num_groups, dims->rope_shared != 0).block /
+         gqla::kBlock * elt;
 }
 
 gqla_status gqla_validate_paged(const gqla_dims* dims, const gqla_paged* paged, void* stream) {
@@ -405,6 +415,7 @@ gqla_status gqla_append_tokens(const gqla_dims* dims, const gqla_paged* paged, c
   a.dr = dims->rope_dim;
   a.dn = dims->nope_dim;
   a.dv = dims->v_dim;
+  a.rope_shared = dims->rope_shared;
   a.rope_theta = rope_theta;
   for (int k = 0; k < dims->rope_dim / 2; ++k)
     a.inv_freq[k] = std::pow(static_cast<double>(rope_theta), -2.0 * k / dims->rope_dim);

@@ -32,6 +32,9 @@ struct AttnParams {
   int32_t dk, dvo;               // key width, value/output width
   int32_t k_ts, k_fs;            // K(t, f) at k_ts * t + k_fs * f (k_slab == 0)
   int32_t k_slab;                // > 0: K in feature slabs of this width (see kv_k_index)
+  int32_t k_own;                 // with a shared RoPE key: K features [0, k_own) in the group
+                                 // chunk, the rest in the block's shared key area (else = dk)
+  int64_t kv_off;                // elements from a block's start to its group 0 chunk
   int32_t v_off, v_half, v_ts, v_fs;   // V(t, f) at v_off + v_half*(t/32) + v_ts*(t%32) + v_fs*f
   float scale;
   int32_t n_split, blocks_per_split;
@@ -54,6 +57,7 @@ struct CombineParams {
 struct ProjParams {
   int32_t rows;                  // B * s_q
   int32_t H, G, dc, dr, dn, dv;
+  int32_t rope_shared;           // expanded layout: RoPE key once per block
 };
 
 // Generic kernels: any dims that fit the LDS budget, fp32 or bf16 data.
@@ -64,6 +68,22 @@ hipError_t launch_generic_absorb_query(const ProjParams& d, const void* q_nope, 
                                        const void* w_uk, void* q_abs, bool bf16, hipStream_t s);
 hipError_t launch_generic_out_proj(const ProjParams& d, const float* o_lat, const void* w_uv,
                                    void* out, bool bf16, hipStream_t s);
+// Element offsets inside one block of the expanded cache (both layouts; see gqla.h).
+struct ExpandedLayout {
+  int64_t block;      // elements per block
+  int64_t rope;       // elements of the shared RoPE key area at the block's start (0 if none)
+  int64_t chunk;      // elements per group chunk
+  int32_t k_feats;    // K features stored in each group chunk (d_qk, or d_n when shared)
+};
+__host__ __device__ inline ExpandedLayout expanded_layout(int dn, int dr, int dv, int G, bool shared) {
+  ExpandedLayout l;
+  l.k_feats = shared ? dn : dn + dr;
+  l.rope = shared ? static_cast<int64_t>(kBlock) * dr : 0;
+  l.chunk = static_cast<int64_t>(kBlock) * (l.k_feats + dv);
+  l.block = l.rope + l.chunk * G;
+  return l;
+}
+
 hipError_t launch_generic_expand(const ProjParams& d, const void* latent, const void* w_uk,
                                  const void* w_uv, const int32_t* block_ids, int64_t n_blocks,
                                  int64_t num_blocks, void* expanded, bool bf16, hipStream_t s);
@@ -76,6 +96,7 @@ struct AppendParams {
   int64_t num_blocks;
   int32_t n_tok, s_q, G;
   int32_t dc, dr, dn, dv;
+  int32_t rope_shared;
   float rope_theta;
   double inv_freq[64];   // rope_theta^(-2k/d_R), k < d_R / 2 (fp64, from the host)
 };

@@ -85,6 +85,9 @@ typedef struct gqla_dims {
   int32_t block_size;   /* tokens per cache block; must be 64 */
   int32_t dtype;        /* gqla_dtype of every "data" tensor */
   float softmax_scale;  /* <= 0 selects 1/sqrt(d_n + d_R) */
+  int32_t rope_shared;  /* expanded-cache layout (GQA path): 0 = the RoPE key in every
+                           group's K; 1 = stored once per block and shared by the groups
+                           (see gqla_expand_cache) */
 } gqla_dims;
 
 /* Paged-cache metadata for one decode batch. */
@@ -145,12 +148,17 @@ gqla_status gqla_out_proj(const gqla_dims* dims, const float* o_lat, const void*
  *   w_uk, w_uv     : data [G][d_n][d_c], [G][d_v][d_c]
  *   block_ids      : device int32 [n_blocks], physical blocks to (re)expand; ids outside
  *                    [0, num_blocks) are skipped
- *   expanded_cache : data [num_blocks][G][64*d_qk + d_v*64]; per (block, group) chunk:
- *                    K = [k_nope | k_rope] in slabs of 32 features: slab s holds
- *                    features [32s, 32s + w_s), w_s = min(32, d_qk - 32s), for all 64
- *                    slots, slot-major (feature f of slot r at 2048*(f/32) + r*w_s + f%32);
- *                    then V in two halves of 32 slots, each feature-major [d_v][32]
+ *   expanded_cache : rope_shared = 0: data [num_blocks][G][64*d_qk + d_v*64]; per (block,
+ *                    group) chunk: K = [k_nope | k_rope] in slabs of 32 features: slab s
+ *                    holds features [32s, 32s + w_s), w_s = min(32, d_qk - 32s), for all
+ *                    64 slots, slot-major (feature f of slot r at 2048*(f/32) + r*w_s +
+ *                    f%32); then V in two halves of 32 slots, each feature-major [d_v][32]
  *                    (feature f of slot r at 64*d_qk + 32*d_v*(r/32) + 32*f + r%32).
+ *                    rope_shared = 1: per block, first the RoPE keys of its 64 slots once
+ *                    ([64*d_R], slabs of 32 as above over the d_R features), then per
+ *                    group a chunk of 64*d_n + d_v*64: k_nope in slabs over the d_n
+ *                    features, then V as above (64*d_n in place of 64*d_qk); a block is
+ *                    64*d_R + G*64*(d_n + d_v) values (gqla_cache_bytes_per_token * 64).
  *                    (With these slabs each wide load of the decode kernel covers
  *                    whole 128-byte lines of a bf16 cache.)
  */
@@ -225,7 +233,8 @@ gqla_status gqla_pick_path(const gqla_dims* dims, int64_t total_ctx, int32_t max
                            float* est_us);
 
 /* Cache bytes per token per layer: latent (d_c + d_R) * elt for the absorb path,
- * G * (d_qk + d_v) * elt for the GQA path; 0 for invalid arguments. */
+ * G * (d_qk + d_v) * elt for the GQA path (G * (d_n + d_v) * elt + d_R * elt with
+ * rope_shared); 0 for invalid arguments. */
 int64_t gqla_cache_bytes_per_token(const gqla_dims* dims, int32_t path);
 
 /* Synchronous debug check of device-side paged metadata: copies block_table and ctx_lens

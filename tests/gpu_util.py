@@ -36,14 +36,16 @@ def torch_dtype(dtype: str):
 class Run:
     """Device copies of one Inputs batch and calls of both GQLA paths."""
 
-    def __init__(self, x, num_splits: int = 0):
+    def __init__(self, x, num_splits: int = 0, rope_shared: bool = False):
         import decode_attention_02_amd as G
         self.G = G
         self.x = x
+        self.rope_shared = rope_shared
         w = x.w
         self.dims = G.Dims(batch=len(x.ctx_lens), num_heads=w.heads, num_groups=w.groups,
                            latent_rank=w.latent, rope_dim=w.rope, nope_dim=w.nope, v_dim=w.v,
-                           s_q=x.s_q, dtype=G.GQLA_BF16 if x.dtype == "bf16" else G.GQLA_F32)
+                           s_q=x.s_q, dtype=G.GQLA_BF16 if x.dtype == "bf16" else G.GQLA_F32,
+                           rope_shared=int(rope_shared))
         self.cache = to_dev(x.latent_cache, x.dtype)
         self.w_uk = to_dev(x.w_uk, x.dtype)
         self.w_uv = to_dev(x.w_uv, x.dtype)
@@ -77,7 +79,7 @@ class Run:
     def expand(self, block_ids=None):
         G, w, x = self.G, self.x.w, self.x
         dt = torch_dtype(x.dtype)
-        per_block = w.groups * 64 * (w.qk + w.v)
+        per_block = expanded_block_values(w.groups, w.qk, w.v, self.rope_shared, w.rope)
         expanded = torch.full((x.num_blocks * per_block,), float("nan"), dtype=dt, device="cuda")
         ids = torch.arange(x.num_blocks, dtype=torch.int32, device="cuda") if block_ids is None else block_ids
         G.gqla_expand_cache(self.dims, self.cache, self.w_uk, self.w_uv, ids, x.num_blocks, expanded)
@@ -95,35 +97,64 @@ class Run:
         return dict(out=to_host(out), lse=to_host(lse), expanded=expanded)
 
 
-def _slab_widths(dqk: int):
-    return [min(32, dqk - s) for s in range(0, dqk, 32)]
+def _slab_widths(n: int):
+    return [min(32, n - s) for s in range(0, n, 32)]
 
 
-def expanded_to_logical(flat: np.ndarray, num_blocks: int, G: int, dqk: int, dv: int):
+def _slabs_to_logical(a: np.ndarray, n_feat: int) -> np.ndarray:
+    """[..., 64 * n_feat] in 32-feature slabs ([64][w] each) -> [..., 64, n_feat]."""
+    parts, off = [], 0
+    for w in _slab_widths(n_feat):
+        parts.append(a[..., off:off + 64 * w].reshape(a.shape[:-1] + (64, w)))
+        off += 64 * w
+    return np.concatenate(parts, axis=-1)
+
+
+def _logical_to_slabs(a: np.ndarray) -> np.ndarray:
+    """[..., 64, n_feat] -> [..., 64 * n_feat] in 32-feature slabs."""
+    n_feat = a.shape[-1]
+    parts, s = [], 0
+    for w in _slab_widths(n_feat):
+        parts.append(a[..., s:s + w].reshape(a.shape[:-2] + (-1,)))
+        s += w
+    return np.concatenate(parts, axis=-1)
+
+
+def expanded_block_values(G: int, dqk: int, dv: int, rope_shared: bool = False, dr: int = 0) -> int:
+    """Values per 64-token block of the expanded cache (both layouts)."""
+    return 64 * (dr + G * (dqk - dr + dv)) if rope_shared else 64 * G * (dqk + dv)
+
+
+def expanded_to_logical(flat: np.ndarray, num_blocks: int, G: int, dqk: int, dv: int,
+                        rope_shared: bool = False, dr: int = 0):
     """Read the documented expanded-cache layout back into K [NB][G][64][dqk] and
     V [NB][G][64][dv] (token-major) for comparison. Per (block, group) chunk: K as
     slabs of 32 features, each [64 slots][width]; then V as two 32-slot halves, each
-    [dv][32]."""
-    chunk = flat.reshape(num_blocks, G, 64 * (dqk + dv))
-    parts, off = [], 0
-    for w in _slab_widths(dqk):
-        parts.append(chunk[:, :, off:off + 64 * w].reshape(num_blocks, G, 64, w))
-        off += 64 * w
-    K = np.concatenate(parts, axis=3)
-    V = chunk[:, :, off:].reshape(num_blocks, G, 2, dv, 32).transpose(0, 1, 2, 4, 3).reshape(num_blocks, G, 64, dv)
+    [dv][32]. With rope_shared the block starts with the RoPE keys once (slabs over d_R)
+    and each group chunk holds only the d_n key features; K is returned with the shared
+    key repeated in every group."""
+    blk = flat.reshape(num_blocks, expanded_block_values(G, dqk, dv, rope_shared, dr))
+    kf = dqk - dr if rope_shared else dqk
+    rope_vals = 64 * dr if rope_shared else 0
+    chunk = blk[:, rope_vals:].reshape(num_blocks, G, 64 * (kf + dv))
+    K = _slabs_to_logical(chunk[:, :, :64 * kf], kf)
+    if rope_shared:
+        rk = _slabs_to_logical(blk[:, :rope_vals], dr)
+        K = np.concatenate([K, np.repeat(rk[:, None], G, axis=1)], axis=-1)
+    V = chunk[:, :, 64 * kf:].reshape(num_blocks, G, 2, dv, 32).transpose(0, 1, 2, 4, 3).reshape(num_blocks, G, 64, dv)
     return K, V
 
 
-def logical_to_expanded(K: np.ndarray, V: np.ndarray) -> np.ndarray:
-    """Inverse of expanded_to_logical."""
+def logical_to_expanded(K: np.ndarray, V: np.ndarray, rope_shared: bool = False, dr: int = 0) -> np.ndarray:
+    """Inverse of expanded_to_logical (with rope_shared, the shared key is group 0's)."""
     NB, G, _, dqk = K.shape
     dv = V.shape[3]
-    parts, s = [], 0
-    for w in _slab_widths(dqk):
-        parts.append(K[:, :, :, s:s + w].reshape(NB, G, -1))
-        s += w
-    parts.append(V.reshape(NB, G, 2, 32, dv).transpose(0, 1, 2, 4, 3).reshape(NB, G, -1))
-    return np.concatenate(parts, axis=2).reshape(-1)
+    kf = dqk - dr if rope_shared else dqk
+    Vh = V.reshape(NB, G, 2, 32, dv).transpose(0, 1, 2, 4, 3).reshape(NB, G, -1)
+    chunks = np.concatenate([_logical_to_slabs(K[..., :kf]), Vh], axis=2).reshape(NB, -1)
+    if rope_shared:
+        chunks = np.concatenate([_logical_to_slabs(K[:, 0, :, kf:]), chunks], axis=1)
+    return chunks.reshape(-1)
 
 
 def oracle_paths(x, seqs=None):

@@ -28,12 +28,12 @@ def _store(a: np.ndarray, dtype: str) -> np.ndarray:
     return f64_to_bf16_bits(a) if dtype == "bf16" else a.astype(np.float32)
 
 
-def _append(name, dtype, s_q, ctx, seed, bad_first=False):
+def _append(name, dtype, s_q, ctx, seed, bad_first=False, rope_shared=False):
     w = workload(name)
     x = generate(w, s_q, batch=len(ctx), ctx_lens=ctx, dtype=dtype, shuffled=True, extra_blocks=2)
     if bad_first:
         x.ctx_lens[0] = s_q - 1   # metadata the append must skip
-    run = Run(x)
+    run = Run(x, 0, rope_shared)
     expanded = run.expand()
     lat0, exp0 = _bits(run.cache), _bits(expanded)
     rng = np.random.default_rng(seed)
@@ -53,9 +53,9 @@ def _append(name, dtype, s_q, ctx, seed, bad_first=False):
     ("dsv3-b64-ctx8k", "bf16", 1, [1, 64, 300, 4096]),
     ("dsv3-b64-ctx8k", "bf16", 4, [5, 66, 130]),
 ])
-@pytest.mark.parametrize("bad_first", [False, True])
-def test_append_writes_exactly_the_new_slots(name, dtype, s_q, ctx, bad_first):
-    x, run, expanded, lat0, exp0, c_new, kr_new = _append(name, dtype, s_q, ctx, 11, bad_first)
+@pytest.mark.parametrize("bad_first,rope_shared", [(False, False), (True, False), (False, True)])
+def test_append_writes_exactly_the_new_slots(name, dtype, s_q, ctx, bad_first, rope_shared):
+    x, run, expanded, lat0, exp0, c_new, kr_new = _append(name, dtype, s_q, ctx, 11, bad_first, rope_shared)
     w = x.w
     lat1, exp1 = _bits(run.cache), _bits(expanded)
     rows = R.append_rows(x.f64(c_new), x.f64(kr_new), x.ctx_lens, s_q, THETA)
@@ -63,10 +63,11 @@ def test_append_writes_exactly_the_new_slots(name, dtype, s_q, ctx, bad_first):
         assert not any(b == 0 for b, _ in rows)
     new = np.zeros(lat1.shape[:2], dtype=bool)
     got_lat = x.f64(lat1.view(np.uint16) if dtype == "bf16" else lat1.view(np.float32))
+    lay = (rope_shared, w.rope)
     K1, V1 = expanded_to_logical(x.f64(exp1.view(np.uint16) if dtype == "bf16" else exp1.view(np.float32)),
-                                 x.num_blocks, w.groups, w.qk, w.v)
+                                 x.num_blocks, w.groups, w.qk, w.v, *lay)
     lat_bits = lat1.reshape(lat1.shape[0], 64, -1)
-    k_bits, _ = expanded_to_logical(exp1, x.num_blocks, w.groups, w.qk, w.v)
+    k_bits, _ = expanded_to_logical(exp1, x.num_blocks, w.groups, w.qk, w.v, *lay)
     worst_rope, worst_kv, kv_scale = 0.0, 0.0, 0.0
     f64w_uk, f64w_uv = x.f64(x.w_uk), x.f64(x.w_uv)
     for (b, t), row in rows.items():
@@ -91,8 +92,8 @@ def test_append_writes_exactly_the_new_slots(name, dtype, s_q, ctx, bad_first):
     # everything else untouched, bit for bit
     lat0r = lat0.reshape(lat1.shape[0], 64, -1)
     assert np.array_equal(lat0r[~new], lat_bits[~new])
-    k0, v0 = expanded_to_logical(exp0, x.num_blocks, w.groups, w.qk, w.v)
-    k1b, v1b = expanded_to_logical(exp1, x.num_blocks, w.groups, w.qk, w.v)
+    k0, v0 = expanded_to_logical(exp0, x.num_blocks, w.groups, w.qk, w.v, *lay)
+    k1b, v1b = expanded_to_logical(exp1, x.num_blocks, w.groups, w.qk, w.v, *lay)
     for g in range(w.groups):
         assert np.array_equal(k0[:, g][~new], k1b[:, g][~new])
         assert np.array_equal(v0[:, g][~new], v1b[:, g][~new])
@@ -103,8 +104,9 @@ def test_append_writes_exactly_the_new_slots(name, dtype, s_q, ctx, bad_first):
     ("llama3-8b-b32-ctx8k", "bf16", 2, [63, 65, 700]),
     ("dsv3-b64-ctx8k", "bf16", 2, [2, 129]),
 ])
-def test_decode_after_append_matches_oracle(name, dtype, s_q, ctx):
-    x, run, expanded, _, _, c_new, kr_new = _append(name, dtype, s_q, ctx, 12)
+@pytest.mark.parametrize("rope_shared", [False, True])
+def test_decode_after_append_matches_oracle(name, dtype, s_q, ctx, rope_shared):
+    x, run, expanded, _, _, c_new, kr_new = _append(name, dtype, s_q, ctx, 12, rope_shared=rope_shared)
     w = x.w
     # The updated sequences, as cached (the key rotated and rounded on the GPU).
     lat = _bits(run.cache).reshape(x.num_blocks, 64, -1)

@@ -32,15 +32,16 @@ def _compare(x, got_a, got_g, seqs, label):
         assert la <= lse_tol and lg <= lse_tol
 
 
-@pytest.mark.parametrize("name,s_q", [("llama3-8b-b32-ctx8k", 1), ("llama3-8b-b32-ctx8k", 2),
-                                      ("dsv3-b64-ctx8k", 1), ("dsv3-b64-ctx8k", 2),
-                                      ("dsv3-b8-ctx32k-64k", 2)])
-def test_fullsize_sampled(name, s_q):
+@pytest.mark.parametrize("name,s_q,rope_shared", [("llama3-8b-b32-ctx8k", 1, False), ("llama3-8b-b32-ctx8k", 2, False),
+                                                  ("dsv3-b64-ctx8k", 1, False), ("dsv3-b64-ctx8k", 2, False),
+                                                  ("dsv3-b8-ctx32k-64k", 2, False), ("llama3-8b-b32-ctx8k", 2, True),
+                                                  ("dsv3-b8-ctx32k-64k", 2, True)])
+def test_fullsize_sampled(name, s_q, rope_shared):
     w = workload(name)
-    log(f"fullsize {name} s_q={s_q}: generating")
+    log(f"fullsize {name} s_q={s_q} rope_shared={rope_shared}: generating")
     x = generate(w, s_q)
     B = len(x.ctx_lens)
-    run = Run(x)
+    run = Run(x, 0, rope_shared)
     log(f"fullsize {name} s_q={s_q}: running both paths (B={B}, max ctx {int(x.ctx_lens.max())})")
     got_a, got_g = run.absorb(), run.gqa()
     del run

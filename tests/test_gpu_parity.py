@@ -35,11 +35,12 @@ def _check_paths(x, got_a, got_g, ref, tol, seqs=None, label=""):
 
 @pytest.mark.parametrize("s_q", [1, 2])
 @pytest.mark.parametrize("num_splits", [0, 1, 3])
-def test_tiny_fp32_matches_oracle(s_q, num_splits):
+@pytest.mark.parametrize("rope_shared", [False, True])
+def test_tiny_fp32_matches_oracle(s_q, num_splits, rope_shared):
     w = workload("tiny-fp32")
     x = generate(w, s_q, batch=4, ctx_lens=[64, s_q, 130, 65], shuffled=True)
-    log(f"tiny-fp32 s_q={s_q} splits={num_splits}")
-    run = Run(x, num_splits)
+    log(f"tiny-fp32 s_q={s_q} splits={num_splits} rope_shared={rope_shared}")
+    run = Run(x, num_splits, rope_shared)
     got_a, got_g = run.absorb(), run.gqa()
     _check_paths(x, got_a, got_g, oracle_paths(x), TOL["f32"], label="tiny-fp32")
 
@@ -71,17 +72,18 @@ def _selection_weights(x, rng):
 
 @pytest.mark.parametrize("name,dtype", [("tiny-fp32", "f32"), ("tiny-fp32", "bf16"),
                                         ("dsv3-b64-ctx8k", "bf16"), ("llama3-8b-b32-ctx8k", "bf16")])
-def test_expand_cache_selection_weights_bit_exact(name, dtype):
+@pytest.mark.parametrize("rope_shared", [False, True])
+def test_expand_cache_selection_weights_bit_exact(name, dtype, rope_shared):
     w = workload(name).with_(dtype=dtype)
     x = generate(w, 1, batch=3, ctx_lens=[64, 100, 3], shuffled=True, extra_blocks=1)
     x.w_uk, x.w_uv = _selection_weights(x, np.random.default_rng(5))
-    log(f"expand selection {name} {dtype}")
-    run = Run(x)
+    log(f"expand selection {name} {dtype} rope_shared={rope_shared}")
+    run = Run(x, 0, rope_shared)
     # expand all blocks but the spare one: it must stay untouched (NaN)
     used = np.unique(x.block_table[x.block_table >= 0]).astype(np.int32)
     ids = torch.from_numpy(used).cuda()
     flat = to_host(run.expand(ids))
-    K, V = expanded_to_logical(flat, x.num_blocks, w.groups, w.qk, w.v)
+    K, V = expanded_to_logical(flat, x.num_blocks, w.groups, w.qk, w.v, rope_shared, w.rope)
     cache = x.f64(x.latent_cache)
     Kr, Vr = R.expand_blocks(cache, used, x.f64(x.w_uk), x.f64(x.w_uv), w.latent)
     spare = sorted(set(range(x.num_blocks)) - set(used.tolist()))
@@ -94,13 +96,14 @@ def test_expand_cache_selection_weights_bit_exact(name, dtype):
 
 
 @pytest.mark.parametrize("name", ["tiny-fp32", "dsv3-b64-ctx8k", "llama3-8b-b32-ctx8k"])
-def test_expand_cache_matches_oracle(name):
+@pytest.mark.parametrize("rope_shared", [False, True])
+def test_expand_cache_matches_oracle(name, rope_shared):
     w = workload(name)
     x = generate(w, 1, batch=2, ctx_lens=[128, 70], shuffled=True)
-    log(f"expand parity {name}")
-    run = Run(x)
+    log(f"expand parity {name} rope_shared={rope_shared}")
+    run = Run(x, 0, rope_shared)
     flat = to_host(run.expand())
-    K, V = expanded_to_logical(flat, x.num_blocks, w.groups, w.qk, w.v)
+    K, V = expanded_to_logical(flat, x.num_blocks, w.groups, w.qk, w.v, rope_shared, w.rope)
     cache = x.f64(x.latent_cache)
     ids = np.arange(x.num_blocks)
     Kr, Vr = R.expand_blocks(cache, ids, x.f64(x.w_uk), x.f64(x.w_uv), w.latent)

@@ -26,11 +26,12 @@ def _ctx(s_q):
 
 @pytest.mark.parametrize("name,s_q", SHAPES)
 @pytest.mark.parametrize("num_splits", [0, 1, 3])
-def test_gqa_decode_matches_oracle(name, s_q, num_splits):
+@pytest.mark.parametrize("rope_shared", [False, True])
+def test_gqa_decode_matches_oracle(name, s_q, num_splits, rope_shared):
     w = workload(name)
     x = generate(w, s_q, batch=6, ctx_lens=_ctx(s_q), shuffled=True, extra_blocks=3)
-    log(f"gqa {name} s_q={s_q} splits={num_splits}")
-    run = Run(x, num_splits)
+    log(f"gqa {name} s_q={s_q} splits={num_splits} rope_shared={rope_shared}")
+    run = Run(x, num_splits, rope_shared)
     got = run.gqa()
     ref = oracle_paths(x)
     for b in ref:
@@ -41,7 +42,8 @@ def test_gqa_decode_matches_oracle(name, s_q, num_splits):
 
 
 @pytest.mark.parametrize("name,s_q", [("dsv3-b64-ctx8k", 2), ("llama3-8b-b32-ctx8k", 2)])
-def test_gqa_decode_on_oracle_expanded_cache(name, s_q):
+@pytest.mark.parametrize("rope_shared", [False, True])
+def test_gqa_decode_on_oracle_expanded_cache(name, s_q, rope_shared):
     """Decode over an expanded cache built by the oracle (rounded to bf16), so the decode
     kernel is checked on its own."""
     from workloads import f64_to_bf16_bits
@@ -49,9 +51,9 @@ def test_gqa_decode_on_oracle_expanded_cache(name, s_q):
     x = generate(w, s_q, batch=3, ctx_lens=[s_q, 200, 64], shuffled=True)
     cache = x.f64(x.latent_cache)
     K, V = R.expand_blocks(np.nan_to_num(cache), np.arange(x.num_blocks), x.f64(x.w_uk), x.f64(x.w_uv), w.latent)
-    flat = f64_to_bf16_bits(logical_to_expanded(K, V))
-    log(f"gqa-on-oracle-cache {name} s_q={s_q}")
-    run = Run(x)
+    flat = f64_to_bf16_bits(logical_to_expanded(K, V, rope_shared, w.rope))
+    log(f"gqa-on-oracle-cache {name} s_q={s_q} rope_shared={rope_shared}")
+    run = Run(x, 0, rope_shared)
     got = run.gqa(expanded=to_dev(flat, "bf16"))
     ref = oracle_paths(x)
     for b in ref:
@@ -76,11 +78,12 @@ def test_gqa_one_token_context_is_value_row():
 
 
 @pytest.mark.parametrize("name,s_q", SHAPES)
-def test_paths_agree_on_gpu(name, s_q):
+@pytest.mark.parametrize("rope_shared", [False, True])
+def test_paths_agree_on_gpu(name, s_q, rope_shared):
     w = workload(name)
     x = generate(w, s_q, batch=3, ctx_lens=[s_q, 333, 1000], shuffled=True)
-    log(f"absorb-vs-gqa {name} s_q={s_q}")
-    run = Run(x)
+    log(f"absorb-vs-gqa {name} s_q={s_q} rope_shared={rope_shared}")
+    run = Run(x, 0, rope_shared)
     a, g = run.absorb()["out"], run.gqa()["out"]
     for b in range(3):
         assert rel_err(a[b], g[b]) <= TOL["bf16"]
