@@ -8,8 +8,12 @@ and prints one JSON line per case plus a markdown table. The shapes are the Deep
 attention layer and its 1/R tensor-parallel head shares (H = 128/R query heads in
 G = 16/R groups, R = 1, 2, 4, 8) and the LLaMA-3-8B layer converted to GQLA.
 
+The GQA path's expanded cache is in the layout that stores the RoPE key once per block
+unless --gqa-layout per-group is given.
+
 Usage: python -m decode_attention_02_amd.crossover [--batch 64] [--ctx 8192] [--sq 1,2,4]
-                                                   [--reps 10] [--out FILE.md]
+                                                   [--reps 10] [--gqa-layout shared-rope|per-group]
+                                                   [--out FILE.md]
 """
 import argparse
 import json
@@ -49,12 +53,12 @@ def _median_us(fn, reps):
     return ts[len(ts) // 2]
 
 
-def run_case(name, s_q, batch, ctx, reps, gen):
+def run_case(name, s_q, batch, ctx, reps, gen, rope_shared=1):
     H, Gr, dn, dv = SHAPES[name]
     nbs = (ctx + 63) // 64
     nb = batch * nbs
     d = L.Dims(batch=batch, num_heads=H, num_groups=Gr, latent_rank=LATENT, rope_dim=ROPE, nope_dim=dn,
-               v_dim=dv, s_q=s_q)
+               v_dim=dv, s_q=s_q, rope_shared=rope_shared)
     table = torch.arange(nb, dtype=torch.int32, device="cuda").reshape(batch, nbs)
     lens = torch.full((batch,), ctx, dtype=torch.int32, device="cuda")
     paged = L.Paged(table, lens, ctx, nb)
@@ -80,7 +84,8 @@ def run_case(name, s_q, batch, ctx, reps, gen):
         L.gqla_out_proj(d, o_lat, w_uv, out)
 
     t_abs = _median_us(absorb, reps)
-    expanded = torch.empty(nb * Gr * 64 * (dn + ROPE + dv), dtype=torch.bfloat16, device="cuda")
+    expanded = torch.empty(nb * 64 * L.gqla_cache_bytes_per_token(d, L.GQLA_PATH_GQA) // 2,
+                           dtype=torch.bfloat16, device="cuda")
     L.gqla_expand_cache(d, latent, w_uk, w_uv, torch.arange(nb, dtype=torch.int32, device="cuda"), nb, expanded)
     first_new = (ctx - s_q) // 64
     tail = table[:, first_new:nbs].reshape(-1).contiguous()
@@ -95,6 +100,7 @@ def run_case(name, s_q, batch, ctx, reps, gen):
     path, est = L.gqla_pick_path(d, batch * ctx, ctx)
     faster = L.GQLA_PATH_GQA if t_gqa < t_abs else L.GQLA_PATH_ABSORB
     return {"shape": name, "heads": H, "groups": Gr, "s_q": s_q, "batch": batch, "ctx": ctx,
+            "gqa_layout": "shared-rope" if rope_shared else "per-group",
             "absorb_us": t_abs, "gqa_us": t_gqa, "faster": ["absorb", "gqa"][faster],
             "gqa_over_absorb": t_abs / t_gqa - 1.0,
             "picked": ["absorb", "gqa"][path], "est_absorb_us": est[0], "est_gqa_us": est[1],
@@ -108,6 +114,7 @@ def main(argv=None):
     ap.add_argument("--sq", default="1,2,4")
     ap.add_argument("--shapes", default=",".join(SHAPES))
     ap.add_argument("--reps", type=int, default=10)
+    ap.add_argument("--gqa-layout", choices=("shared-rope", "per-group"), default="shared-rope")
     ap.add_argument("--out", default=None)
     a = ap.parse_args(argv)
     gen = torch.Generator(device="cuda")
@@ -115,7 +122,7 @@ def main(argv=None):
     rows = []
     for name in a.shapes.split(","):
         for s_q in (int(v) for v in a.sq.split(",")):
-            r = run_case(name, s_q, a.batch, a.ctx, a.reps, gen)
+            r = run_case(name, s_q, a.batch, a.ctx, a.reps, gen, int(a.gqa_layout == "shared-rope"))
             rows.append(r)
             print(json.dumps(r), flush=True)
     lines = ["| shape | H | G | s_q | absorb us | GQA us | faster | GQA gain | picked | est absorb / GQA us | picked vs best |",

@@ -22,7 +22,9 @@ namespace gqla {
 struct Mi355xRates {
   double absorb_bw = 5.0e12;      // absorb decode latent streaming, B/s (tile copies into LDS)
   double absorb_mfma = 0.65e15;   // absorb decode when MFMA/LDS-bound, flop/s
-  double gqa_bw = 6.4e12;         // GQA decode expanded-cache streaming, B/s
+  double gqa_bw = 6.4e12;         // GQA decode expanded-cache streaming, B/s (per-group layout)
+  double gqa_shared_bw = 6.0e12;  // same, RoPE key once per block (of the smaller byte count:
+                                  // groups that drift apart fetch the shared key again)
   double gqa_mfma = 1.0e15;       // GQA decode padded MFMA work, flop/s
   double expand_mfma = 0.35e15;   // cache expansion, flop/s
   double proj_mfma = 0.2e15;      // absorbed-query and value projections, flop/s
@@ -50,10 +52,11 @@ PathEstimate estimate_paths(const gqla_dims* d, int64_t total_ctx, int n_split_a
   if (n_split_abs > 1) t_abs += r.launch_us + us(rows * n_split_abs * dc * 4.0 / r.combine_bw);
 
   // GQA: expansion of the blocks holding the new tokens, grouped decode, (combine).
-  const double gqa_bytes = tok * G * (dqk + dv) * elt;
+  const double gqa_bytes = tok * (d->rope_shared ? G * (dn + dv) + dr : G * (dqk + dv)) * elt;
   const double tile_rows = 16.0 * std::ceil(H / G * s / 16.0);
   const double gqa_flops = tok * G * tile_rows * 2.0 * (dqk + dv);
-  double t_gqa = std::max(us(gqa_bytes / r.gqa_bw), us(gqa_flops / r.gqa_mfma));
+  const double gqa_bw = d->rope_shared ? r.gqa_shared_bw : r.gqa_bw;
+  double t_gqa = std::max(us(gqa_bytes / gqa_bw), us(gqa_flops / r.gqa_mfma));
   const double new_blocks = B * (1.0 + (s - 1.0) / kBlock);
   t_gqa += r.launch_us + us(new_blocks * G * kBlock * (dn + dv) * dc * 2.0 / r.expand_mfma);
   if (n_split_gqa > 1) t_gqa += r.launch_us + us(B * s * H * n_split_gqa * dv * 4.0 / r.combine_bw);

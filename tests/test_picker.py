@@ -7,9 +7,9 @@ import decode_attention_02_amd as G
 from decode_attention_02_amd import _lib
 
 
-def dims(H=128, Gr=16, s_q=1, B=64, dn=128, dv=128):
+def dims(H=128, Gr=16, s_q=1, B=64, dn=128, dv=128, rope_shared=0):
     return G.Dims(batch=B, num_heads=H, num_groups=Gr, latent_rank=512, rope_dim=64, nope_dim=dn,
-                  v_dim=dv, s_q=s_q)
+                  v_dim=dv, s_q=s_q, rope_shared=rope_shared)
 
 
 def test_rejects_bad_context_totals():
@@ -49,3 +49,13 @@ def test_clear_cut_choices():
     assert G.gqla_pick_path(dims(s_q=1), 64 * 8192, 8192)[0] == G.GQLA_PATH_ABSORB
     # sixteen query rows: the absorb path's head-products dominate
     assert G.gqla_pick_path(dims(s_q=16), 64 * 8192, 8192)[0] == G.GQLA_PATH_GQA
+
+
+def test_shared_rope_layout_lowers_only_the_gqa_estimate():
+    # LLaMA-3-8B shape: the RoPE key once per block instead of once per group cuts the
+    # expanded bytes per token from 8 * 256 to 8 * 192 + 64 values (-22%)
+    base = dict(H=32, Gr=8, s_q=2, B=32, dn=64, dv=128)
+    _, (a0, g0) = G.gqla_pick_path(dims(**base), 32 * 8192, 8192)
+    _, (a1, g1) = G.gqla_pick_path(dims(**base, rope_shared=1), 32 * 8192, 8192)
+    assert a1 == a0
+    assert 0.7 * g0 < g1 < 0.95 * g0
