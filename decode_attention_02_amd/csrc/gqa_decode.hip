@@ -178,7 +178,8 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_split(AttnParams p) {
       const bf16_t* rrow = rk + tok * kSlab + 8 * grp;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        f.k[tt][ks] = load8_stream(ks < KSN ? krow + ks * kBlock * kSlab : rrow + (ks - KSN) * kBlock * kSlab);
+        f.k[tt][ks] = ks < KSN ? load8_stream(krow + ks * kBlock * kSlab)
+                               : load8(rrow + (ks - KSN) * kBlock * kSlab);
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
