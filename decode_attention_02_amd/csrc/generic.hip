@@ -162,7 +162,9 @@ hipError_t launch_generic_attn(const AttnParams& p, bool bf16, hipStream_t s) {
 // Merge split partials: o = sum_s w_s o_s / sum_s w_s, w_s = exp(lse_s - max lse);
 // lse = max + ln sum w. A NaN partial (bad metadata) makes the row NaN. Every thread
 // derives the weights itself from the row's lse values (L2-resident), then handles four
-// consecutive features with 16-byte loads.
+// consecutive features with 16-byte loads, eight splits at a time: the loads of a batch
+// are issued together and an empty split (lse = -inf) is skipped by its weight, not by a
+// branch around its load.
 __global__ __launch_bounds__(128) void combine_splits(CombineParams c) {
   const int64_t row = blockIdx.x;
   const float* lse = c.ws_lse + row * c.n_split;
@@ -182,14 +184,24 @@ __global__ __launch_bounds__(128) void combine_splits(CombineParams c) {
   const float inv = 1.f / tot;
   const float* o = c.ws_o + row * c.n_split * c.dvo;
   if ((c.dvo & 3) == 0) {
+    constexpr int kBatch = 8;
     for (int f = 4 * threadIdx.x; f < c.dvo; f += 4 * blockDim.x) {
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int s = 0; s < c.n_split; ++s) {
-        const float l = lse[s];
-        if (l == -INFINITY) continue;
-        const float w = expf(l - m);
-        const float4 v = *reinterpret_cast<const float4*>(o + static_cast<int64_t>(s) * c.dvo + f);
-        acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
+      for (int s0 = 0; s0 < c.n_split; s0 += kBatch) {
+        float4 v[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j)
+          if (s0 + j < c.n_split) v[j] = *reinterpret_cast<const float4*>(o + static_cast<int64_t>(s0 + j) * c.dvo + f);
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          if (s0 + j < c.n_split) {
+            const float l = lse[s0 + j];
+            if (l != -INFINITY) {
+              const float w = expf(l - m);
+              acc.x += w * v[j].x; acc.y += w * v[j].y; acc.z += w * v[j].z; acc.w += w * v[j].w;
+            }
+          }
+        }
       }
       const float r[4] = {acc.x, acc.y, acc.z, acc.w};
       for (int k = 0; k < 4; ++k) store_out(c.out, c.out_kind, row * c.dvo + f + k, nan_row ? nan_f32() : r[k] * inv);
