@@ -181,6 +181,38 @@ def out_projection(o_lat, w_uv):
     return out
 
 
+# ------------------------------------------------------ output side: W_O and its fold
+
+def hidden_projection(out, w_o):
+    """The module's output projection ([MODULE] forward(), its last step): the heads'
+    outputs laid side by side head-major (feature h*d_v + v of the concatenation is value
+    v of head h) and multiplied by W_O^T, W_O being [hidden][H*d_v]:
+    y[.., n] = sum_h sum_v W_O[n, h*d_v + v] out[.., h, v]."""
+    flat = out.reshape(out.shape[:-2] + (out.shape[-2] * out.shape[-1],))
+    return flat @ w_o.T
+
+
+def fold_out_weight(w_o, w_uv, num_heads):
+    """W_O with every head's value up-projection folded in. On the absorb path (MLA's
+    absorbed form, [GQLA-A]) W_UV^g acts on each head's latent output and W_O right after
+    it; both are linear, so their product can be formed once (reading: the pages name the
+    absorbed form but not this step; it is associativity of the two products):
+    W_fold[n, h*d_c + c] = sum_v W_O[n, h*d_v + v] W_UV^g[v, c]."""
+    G, d_v, d_c = w_uv.shape
+    hidden = w_o.shape[0]
+    w_fold = np.zeros((hidden, num_heads * d_c))
+    for h in range(num_heads):
+        w_fold[:, h * d_c:(h + 1) * d_c] = w_o[:, h * d_v:(h + 1) * d_v] @ w_uv[head_group(h, num_heads, G)]
+    return w_fold
+
+
+def folded_hidden_projection(o_lat, w_fold):
+    """The absorb path's output side with the folded weight: the heads' latent outputs
+    laid side by side head-major and multiplied by W_fold^T."""
+    flat = o_lat.reshape(o_lat.shape[:-2] + (o_lat.shape[-2] * o_lat.shape[-1],))
+    return flat @ w_fold.T
+
+
 # ------------------------------------------------------------------- path (b): GQA
 
 def expand_latent(c, kr, w_uk, w_uv):

@@ -390,3 +390,58 @@ def test_append_rows_positions_and_skips():
     assert np.array_equal(rows[(2, 63)][:8], c[2, 1])
     assert np.allclose(rows[(0, 8)][8:], R.rope_at(kr[0, 0], 8))
     assert not np.allclose(rows[(0, 8)][8:], kr[0, 0])
+
+
+# ------------------------------------------------------------------ output-side pins
+
+def _out_side_inputs(seed=5, B=2, H=8, G=2, d_v=6, d_c=10, hidden=12):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((B, H, d_v)), rng.standard_normal((B, H, d_c)),
+            rng.standard_normal((G, d_v, d_c)), rng.standard_normal((hidden, H * d_v)))
+
+
+def test_hidden_projection_is_the_modules_linear_layer():
+    """The module's last step: attention output of shape (b, H, s, head_dim) transposed to
+    (b, s, H, head_dim), flattened and passed through a bias-free Linear(H*head_dim,
+    hidden). Re-done here with the module's own torch operations on s = 1."""
+    out, _, _, w_o = _out_side_inputs()
+    t = torch.from_numpy(out)[:, :, None, :]                         # (b, H, s=1, d_v)
+    flat = t.transpose(1, 2).contiguous().view(out.shape[0], 1, -1)
+    lin = torch.nn.Linear(w_o.shape[1], w_o.shape[0], bias=False).double()
+    with torch.no_grad():
+        lin.weight.copy_(torch.from_numpy(w_o))
+        ref = lin(flat)[:, 0].numpy()
+    assert _rel(R.hidden_projection(out, w_o), ref) < 1e-14
+
+
+def test_hidden_projection_head_major_order():
+    """With W_O the identity (hidden = H*d_v) the projection returns feature h*d_v + v =
+    value v of head h; a permutation moves exactly one value per output."""
+    out, _, _, _ = _out_side_inputs(hidden=8 * 6)
+    B, H, d_v = out.shape
+    y = R.hidden_projection(out, np.eye(H * d_v))
+    for h in range(H):
+        for v in range(d_v):
+            assert y[1, h * d_v + v] == out[1, h, v]
+    perm = np.random.default_rng(1).permutation(H * d_v)
+    y = R.hidden_projection(out, np.eye(H * d_v)[perm])
+    for n in range(H * d_v):
+        assert y[0, n] == out[0, perm[n] // d_v, perm[n] % d_v]
+
+
+def test_fold_equals_value_then_output_projection():
+    """Folding W_UV^g into W_O changes nothing: W_fold applied to the latent outputs equals
+    W_O applied after W_UV^g, and a brute-force sum over heads, values and latent features
+    gives the same folded weight."""
+    _, o_lat, w_uv, w_o = _out_side_inputs()
+    H = o_lat.shape[1]
+    w_fold = R.fold_out_weight(w_o, w_uv, H)
+    a = R.folded_hidden_projection(o_lat, w_fold)
+    b = R.hidden_projection(R.out_projection(o_lat, w_uv), w_o)
+    assert _rel(a, b) < 1e-12
+    G, d_v, d_c = w_uv.shape
+    for n in (0, 7):
+        for h in (0, 3, 5, 7):
+            for c in (0, 9):
+                ref = sum(w_o[n, h * d_v + v] * w_uv[h // (H // G), v, c] for v in range(d_v))
+                assert abs(w_fold[n, h * d_c + c] - ref) < 1e-12
