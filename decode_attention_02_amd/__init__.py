@@ -7,6 +7,7 @@ the library has not been built.
 from ._lib import (  # noqa: F401
     EXPORTED, GQLA_BF16, GQLA_F32, GQLA_PATH_ABSORB, GQLA_PATH_GQA, Dims, GqlaError, Paged,
     gqla_absorb_query, gqla_append_tokens, gqla_cache_bytes_per_token, gqla_decode_absorb, gqla_decode_gqa,
-    gqla_expand_cache, gqla_num_splits, gqla_out_proj, gqla_pick_path, gqla_validate_paged, gqla_version,
+    gqla_expand_cache, gqla_fold_out_weight, gqla_num_splits, gqla_out_hidden, gqla_out_proj, gqla_pick_path,
+    gqla_validate_paged, gqla_version,
     gqla_workspace_bytes, LIB, LIB_PATH,
 )

@@ -21,7 +21,8 @@ GQLA_PATH_ABSORB, GQLA_PATH_GQA = 0, 1
 EXPORTED = ("gqla_absorb_query", "gqla_decode_absorb", "gqla_out_proj", "gqla_expand_cache",
             "gqla_decode_gqa", "gqla_num_splits", "gqla_workspace_bytes",
             "gqla_cache_bytes_per_token", "gqla_validate_paged", "gqla_status_string",
-            "gqla_last_error", "gqla_version", "gqla_pick_path", "gqla_append_tokens")
+            "gqla_last_error", "gqla_version", "gqla_pick_path", "gqla_append_tokens",
+            "gqla_out_hidden", "gqla_fold_out_weight")
 
 
 class GqlaError(RuntimeError):
@@ -63,6 +64,8 @@ def _load() -> ctypes.CDLL:
         "gqla_validate_paged": [D, P, vp],
         "gqla_pick_path": [D, i64, i32, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_float)],
         "gqla_append_tokens": [D, P, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp],
+        "gqla_out_hidden": [D, i32, i32, vp, vp, vp, vp],
+        "gqla_fold_out_weight": [D, i32, vp, vp, vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -208,6 +211,20 @@ def gqla_append_tokens(dims: Dims, paged: Paged, c_new, kr_new, rope_theta: floa
     _check(LIB.gqla_append_tokens(ctypes.byref(d), ctypes.byref(p), _ptr(c_new), _ptr(kr_new), ctypes.c_float(rope_theta),
                                   _ptr(w_uk), _ptr(w_uv), _ptr(latent_cache), _ptr(expanded_cache), _stream(stream)),
            "gqla_append_tokens")
+
+
+def gqla_out_hidden(dims: Dims, hidden: int, folded: bool, x, w, y, stream=None) -> None:
+    """y = x W^T: W_O over the heads' outputs (folded=False) or the folded weight over the
+    absorb path's latent outputs (folded=True)."""
+    d = dims.c()
+    _check(LIB.gqla_out_hidden(ctypes.byref(d), hidden, int(bool(folded)), _ptr(x), _ptr(w), _ptr(y), _stream(stream)),
+           "gqla_out_hidden")
+
+
+def gqla_fold_out_weight(dims: Dims, hidden: int, w_o, w_uv, w_fold, stream=None) -> None:
+    d = dims.c()
+    _check(LIB.gqla_fold_out_weight(ctypes.byref(d), hidden, _ptr(w_o), _ptr(w_uv), _ptr(w_fold), _stream(stream)),
+           "gqla_fold_out_weight")
 
 
 def gqla_pick_path(dims: Dims, total_ctx: int, max_ctx: int):

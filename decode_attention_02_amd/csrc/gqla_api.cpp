@@ -424,4 +424,31 @@ gqla_status gqla_append_tokens(const gqla_dims* dims, const gqla_paged* paged, c
   return e == hipSuccess ? GQLA_OK : hip_fail(e, "append launch");
 }
 
+gqla_status gqla_out_hidden(const gqla_dims* dims, int32_t hidden, int32_t folded, const void* x,
+                            const void* w, void* y, void* stream) {
+  gqla_status st = check_dims(dims);
+  if (st != GQLA_OK) return st;
+  if (hidden < 1 || hidden > 65535) return fail(GQLA_ERR_INVALID_ARG, "hidden must be in [1, 65535], got %d", hidden);
+  if (folded != 0 && folded != 1) return fail(GQLA_ERR_INVALID_ARG, "folded must be 0 or 1");
+  if (!x || !w || !y) return fail(GQLA_ERR_INVALID_ARG, "null tensor pointer");
+  const int64_t rows = static_cast<int64_t>(dims->batch) * dims->s_q;
+  const int64_t k = static_cast<int64_t>(dims->num_heads) * (folded ? dims->latent_rank : dims->v_dim);
+  if (rows > 0x7fffffff || k > 0x7fffffff) return fail(GQLA_ERR_INVALID_ARG, "output side too large");
+  const bool bf16 = dims->dtype == GQLA_BF16;
+  hipError_t e = gqla::launch_out_hidden(x, folded == 1 || !bf16, w, y, static_cast<int>(rows), hidden,
+                                         static_cast<int>(k), bf16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GQLA_OK : hip_fail(e, "output projection launch");
+}
+
+gqla_status gqla_fold_out_weight(const gqla_dims* dims, int32_t hidden, const void* w_o, const void* w_uv,
+                                 void* w_fold, void* stream) {
+  gqla_status st = check_dims(dims);
+  if (st != GQLA_OK) return st;
+  if (hidden < 1 || hidden > 65535) return fail(GQLA_ERR_INVALID_ARG, "hidden must be in [1, 65535], got %d", hidden);
+  if (!w_o || !w_uv || !w_fold) return fail(GQLA_ERR_INVALID_ARG, "null tensor pointer");
+  hipError_t e = gqla::launch_fold_out_weight(proj_params(dims), hidden, w_o, w_uv, w_fold, dims->dtype == GQLA_BF16,
+                                              static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GQLA_OK : hip_fail(e, "weight fold launch");
+}
+
 }  // extern "C"

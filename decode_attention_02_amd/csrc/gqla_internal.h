@@ -68,6 +68,12 @@ hipError_t launch_generic_absorb_query(const ProjParams& d, const void* q_nope, 
                                        const void* w_uk, void* q_abs, bool bf16, hipStream_t s);
 hipError_t launch_generic_out_proj(const ProjParams& d, const float* o_lat, const void* w_uv,
                                    void* out, bool bf16, hipStream_t s);
+// Output side: y[M][N] = x[M][K] w[N][K]^T (x fp32 or the data type), and the fold of
+// W_UV^g into W_O.
+hipError_t launch_out_hidden(const void* x, bool x_f32, const void* w, void* y, int M, int N, int K, bool bf16,
+                             hipStream_t s);
+hipError_t launch_fold_out_weight(const ProjParams& p, int hidden, const void* w_o, const void* w_uv, void* w_fold,
+                                  bool bf16, hipStream_t s);
 // Element offsets inside one block of the expanded cache (both layouts; see gqla.h).
 struct ExpandedLayout {
   int64_t block;      // elements per block

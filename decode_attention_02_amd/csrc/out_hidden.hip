@@ -1,0 +1,245 @@
+// Output side of the attention layer on gfx950: the projection W_O that follows the heads
+// (the module's bias-free out_proj over the head-major concatenation of the heads'
+// outputs, "gqla_attn.py" module source, GQLAAttention.forward), and, for the MQA-absorb
+// path, W_O with each head's value up-projection W_UV^g folded in.
+//
+//   unfolded:  y[r][n] = sum_{h,v} W_O[n][h*d_v + v]    out[r][h][v]     (out: bf16)
+//   folded:    y[r][n] = sum_{h,c} W_fold[n][h*d_c + c] o_lat[r][h][c]   (o_lat: fp32)
+//   fold:      W_fold[n][h*d_c + c] = sum_v W_O[n][h*d_v + v] W_UV^g[v][c]   (once per model)
+//
+// At decode there are few rows (B * s_q) against a large weight (hidden x H*d_v or
+// hidden x H*d_c), so the product is bound by streaming the weight from HBM once. Each
+// workgroup owns 16, 32 or 64 output features (rows of the weight) and splits the
+// contraction over its 4 waves; every wave streams its part of those rows with 16-byte
+// loads (the MFMA A operand straight from global memory, two chunks in flight) and reads
+// the rows' inputs, which every workgroup shares, from L2, each input operand feeding
+// one MFMA per weight tile. The 4 partial results are summed through LDS. An fp32 input is split into bf16 high and low parts (two MFMAs), which
+// keeps the product close to fp32 accuracy.
+#include "device_common.h"
+#include "gqla_internal.h"
+
+namespace gqla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;        // waves per workgroup, each a quarter of the contraction
+constexpr int kU = 4;            // k-steps (of 32) per load chunk (2 for fp32 inputs)
+
+// Weight rows n0 .. n0 + 16*NTW, input rows m0 .. m0 + 16*MT. Each input operand feeds
+// NTW MFMAs and each weight operand MT (the weight is the HBM stream; the inputs, read by
+// every workgroup, come from L2, so NTW >= MT keeps their traffic at or below the
+// weight's).
+template <bool XF32, int MT, int NTW>
+__global__ __launch_bounds__(kWaves * 64) void hidden_gemm(const void* x, const bf16_t* w, bf16_t* y, int M, int N,
+                                                            int K) {
+  __shared__ f32x4 part[kWaves][NTW][MT][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int n0 = blockIdx.x * 16 * NTW;
+  const int m0 = blockIdx.y * 16 * MT;
+  const int kw = K / kWaves;                    // a multiple of 32 (K % 128 == 0)
+  const int kbeg = wave * kw;
+  const int steps = kw / 32;
+  // A operand of weight tile j: row n0 + 16*j + col, features k + 8*grp .. +8.
+  const bf16_t* wrow = w + static_cast<int64_t>(n0 + col) * K + kbeg + 8 * grp;
+  const int64_t wtile = static_cast<int64_t>(16) * K;
+  // B operand: input row m (clamped to the last row; only live rows are stored).
+  int64_t xrow[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) xrow[t] = static_cast<int64_t>(min(m0 + 16 * t + col, M - 1)) * K + kbeg + 8 * grp;
+
+  f32x4 acc[NTW][MT];
+#pragma unroll
+  for (int j = 0; j < NTW; ++j)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // One chunk = U k-steps of the weight tiles and of the input rows, loaded together.
+  constexpr int U = XF32 ? 2 : kU;
+  constexpr int XV = XF32 ? 2 : 1;               // 16-byte loads per input operand
+  struct Chunk {
+    bf16x8 w[U][NTW];
+    f32x4 x[U][MT][XV];                         // bf16 inputs use the bits of x[..][0]
+  };
+  auto load = [&](Chunk& c, int s0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = s0 + u < steps;
+#pragma unroll
+      for (int j = 0; j < NTW; ++j)
+        c.w[u][j] = ok ? *reinterpret_cast<const bf16x8*>(wrow + j * wtile + 32 * (s0 + u)) : bf16x8{};
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        if constexpr (XF32) {
+          const float* xp = static_cast<const float*>(x) + xrow[t] + 32 * (s0 + u);
+          c.x[u][t][0] = ok ? *reinterpret_cast<const f32x4*>(xp) : f32x4{};
+          c.x[u][t][1] = ok ? *reinterpret_cast<const f32x4*>(xp + 4) : f32x4{};
+        } else {
+          const bf16_t* xp = static_cast<const bf16_t*>(x) + xrow[t] + 32 * (s0 + u);
+          c.x[u][t][0] = ok ? *reinterpret_cast<const f32x4*>(xp) : f32x4{};
+        }
+      }
+    }
+  };
+  auto mma = [&](const Chunk& c) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        if constexpr (XF32) {
+          bf16x8 hi, lo;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const float v = c.x[u][t][k >> 2][k & 3];
+            const __bf16 h = static_cast<__bf16>(v);
+            hi[k] = h;
+            lo[k] = static_cast<__bf16>(v - static_cast<float>(h));
+          }
+#pragma unroll
+          for (int j = 0; j < NTW; ++j) {
+            acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.w[u][j], hi, acc[j][t], 0, 0, 0);
+            acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.w[u][j], lo, acc[j][t], 0, 0, 0);
+          }
+        } else {
+          const bf16x8 xv = __builtin_bit_cast(bf16x8, c.x[u][t][0]);
+#pragma unroll
+          for (int j = 0; j < NTW; ++j) acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c.w[u][j], xv, acc[j][t], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // Two chunks in flight: the next chunk's loads go out before this one is used.
+  Chunk c0, c1;
+  load(c0, 0);
+  for (int s0 = 0; s0 < steps; s0 += 2 * U) {
+    load(c1, s0 + U);
+    mma(c0);
+    if (s0 + U >= steps) break;
+    load(c0, s0 + 2 * U);
+    mma(c1);
+  }
+
+  // D[n][m]: lane holds features n0 + 16*j + 4*grp + r of row m0 + 16*t + col. Sum the
+  // waves' shares; wave j' stores weight tiles j = j', j' + 4, ...
+#pragma unroll
+  for (int j = 0; j < NTW; ++j)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) part[wave][j][t][lane] = acc[j][t];
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) {
+    if (j % kWaves != wave) continue;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      f32x4 sum = part[0][j][t][lane];
+#pragma unroll
+      for (int v = 1; v < kWaves; ++v) sum += part[v][j][t][lane];
+      const int m = m0 + 16 * t + col;
+      if (m < M) {
+        bf16_t packed[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) packed[r] = f32_to_bf16(sum[r]);
+        *reinterpret_cast<uint2*>(y + static_cast<int64_t>(m) * N + n0 + 16 * j + 4 * grp) =
+            *reinterpret_cast<uint2*>(packed);
+      }
+    }
+  }
+}
+
+template <bool XF32, int MT, int NTW>
+hipError_t launch_mt(const void* x, const void* w, void* y, int M, int N, int K, hipStream_t s) {
+  const dim3 grid(N / (16 * NTW), (M + 16 * MT - 1) / (16 * MT));
+  hidden_gemm<XF32, MT, NTW><<<grid, kWaves * 64, 0, s>>>(x, static_cast<const bf16_t*>(w), static_cast<bf16_t*>(y),
+                                                          M, N, K);
+  return hipGetLastError();
+}
+
+// Row tiles per pass MT = 1, 2 or 4 (more rows take several passes over the weight, run
+// side by side). Weight tiles per wave NTW up to MT, but no fewer than 256 workgroups
+// (one per CU) over the output width: at hidden = 4096 that leaves NTW = 1.
+template <bool XF32, int MT>
+hipError_t launch_ntw(const void* x, const void* w, void* y, int M, int N, int K, hipStream_t s) {
+  if constexpr (MT >= 4) {
+    if (N % 64 == 0 && N / 64 >= kNumCUs) return launch_mt<XF32, MT, 4>(x, w, y, M, N, K, s);
+  }
+  if constexpr (MT >= 2) {
+    if (N % 32 == 0 && N / 32 >= kNumCUs) return launch_mt<XF32, MT, 2>(x, w, y, M, N, K, s);
+  }
+  return launch_mt<XF32, MT, 1>(x, w, y, M, N, K, s);
+}
+
+template <bool XF32>
+hipError_t launch_x(const void* x, const void* w, void* y, int M, int N, int K, hipStream_t s) {
+  if (M <= 16) return launch_ntw<XF32, 1>(x, w, y, M, N, K, s);
+  if (M <= 32) return launch_ntw<XF32, 2>(x, w, y, M, N, K, s);
+  return launch_ntw<XF32, 4>(x, w, y, M, N, K, s);
+}
+
+// Generic: one thread per output, fp32 accumulation; any sizes, fp32 or bf16 data.
+template <typename T, typename TX>
+__global__ __launch_bounds__(256) void generic_hidden(const TX* x, const T* w, T* y, int M, int N, int K) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= static_cast<int64_t>(M) * N) return;
+  const int m = static_cast<int>(i / N), n = static_cast<int>(i % N);
+  float acc = 0.f;
+  for (int k = 0; k < K; ++k)
+    acc += Elt<TX>::load(x, static_cast<int64_t>(m) * K + k) * Elt<T>::load(w, static_cast<int64_t>(n) * K + k);
+  Elt<T>::store(y, i, acc);
+}
+
+// W_fold[n][h*d_c + c] = sum_v W_O[n][h*d_v + v] W_UV^g[v][c]; one thread per element,
+// threads along c (coalesced W_UV reads, W_O broadcast).
+template <typename T>
+__global__ __launch_bounds__(256) void fold_kernel(ProjParams d, int hidden, const T* w_o, const T* w_uv, T* w_fold) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  const int h = blockIdx.y;
+  const int n = blockIdx.z;
+  if (c >= d.dc) return;
+  const int g = h / (d.H / d.G);
+  const int64_t wo = static_cast<int64_t>(n) * d.H * d.dv + static_cast<int64_t>(h) * d.dv;
+  const int64_t wu = static_cast<int64_t>(g) * d.dv * d.dc + c;
+  float acc = 0.f;
+  for (int v = 0; v < d.dv; ++v) acc += Elt<T>::load(w_o, wo + v) * Elt<T>::load(w_uv, wu + static_cast<int64_t>(v) * d.dc);
+  Elt<T>::store(w_fold, static_cast<int64_t>(n) * d.H * d.dc + static_cast<int64_t>(h) * d.dc + c, acc);
+}
+
+}  // namespace
+
+hipError_t launch_out_hidden(const void* x, bool x_f32, const void* w, void* y, int M, int N, int K, bool bf16,
+                             hipStream_t s) {
+  if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
+  if (bf16 && N % 16 == 0 && K % (32 * kWaves) == 0)
+    return x_f32 ? launch_x<true>(x, w, y, M, N, K, s) : launch_x<false>(x, w, y, M, N, K, s);
+  const int64_t n = static_cast<int64_t>(M) * N;
+  const unsigned blocks = static_cast<unsigned>((n + 255) / 256);
+  if (bf16) {
+    if (x_f32)
+      generic_hidden<bf16_t, float><<<blocks, 256, 0, s>>>(static_cast<const float*>(x), static_cast<const bf16_t*>(w),
+                                                           static_cast<bf16_t*>(y), M, N, K);
+    else
+      generic_hidden<bf16_t, bf16_t><<<blocks, 256, 0, s>>>(static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(w),
+                                                            static_cast<bf16_t*>(y), M, N, K);
+  } else {
+    generic_hidden<float, float><<<blocks, 256, 0, s>>>(static_cast<const float*>(x), static_cast<const float*>(w),
+                                                        static_cast<float*>(y), M, N, K);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fold_out_weight(const ProjParams& p, int hidden, const void* w_o, const void* w_uv, void* w_fold,
+                                  bool bf16, hipStream_t s) {
+  const dim3 grid((p.dc + 255) / 256, p.H, hidden);
+  if (bf16)
+    fold_kernel<bf16_t><<<grid, 256, 0, s>>>(p, hidden, static_cast<const bf16_t*>(w_o), static_cast<const bf16_t*>(w_uv),
+                                             static_cast<bf16_t*>(w_fold));
+  else
+    fold_kernel<float><<<grid, 256, 0, s>>>(p, hidden, static_cast<const float*>(w_o), static_cast<const float*>(w_uv),
+                                            static_cast<float*>(w_fold));
+  return hipGetLastError();
+}
+
+}  // namespace gqla

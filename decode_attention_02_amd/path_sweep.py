@@ -5,7 +5,8 @@ For each workload and query-row count it times, on random data of the workload's
   absorb: gqla_absorb_query -> gqla_decode_absorb (+ split combine) -> gqla_out_proj
   GQA:    gqla_decode_gqa (+ split combine) over an expanded cache that is already resident
 and, separately, the per-token cost of the append path (gqla_append_tokens of the s_q new
-tokens of every sequence, latent rows + RoPE + their expansion into the groups).
+tokens of every sequence, latent rows + RoPE + their expansion into the groups) and the
+output side after the heads (W_O, or W_O with W_UV^g folded in for the absorb path).
 Every timed call is preceded by an untimed read of 1 GiB, so the 256 MiB last-level cache
 holds none of the cache being read (a read, not a write: the write-back of a dirty flush
 buffer would land inside the timed call); the median and the best of the timed calls are
@@ -204,11 +205,56 @@ def run_workload(name, reps, gen, flush, rope_shared=1):
     return rows
 
 
+def run_output_side(name, reps, gen, flush, s_q=1):
+    """The layer's output side after each path at hidden = H * d_v (the module's size):
+    absorb: gqla_out_proj (W_UV^g) then W_O, or W_O with W_UV^g folded in, over the fp32
+    latent outputs; the GQA path needs only W_O. Weight bytes streamed per call are
+    reported as GB/s."""
+    from workloads import workload
+    w = workload(name)
+    if w.dtype != "bf16":
+        return []
+    B, H = w.batch, w.heads
+    hidden = H * w.v
+    d = L.Dims(batch=B, num_heads=H, num_groups=w.groups, latent_rank=w.latent, rope_dim=w.rope,
+               nope_dim=w.nope, v_dim=w.v, s_q=s_q)
+    dt = torch.bfloat16
+    w_o = torch.empty(hidden, H * w.v, dtype=dt, device="cuda")
+    w_uv = torch.empty(w.groups, w.v, w.latent, dtype=dt, device="cuda")
+    _fill(w_o, gen, (H * w.v) ** -0.5)
+    _fill(w_uv, gen, w.latent ** -0.5)
+    w_fold = torch.empty(hidden, H * w.latent, dtype=dt, device="cuda")
+    L.gqla_fold_out_weight(d, hidden, w_o, w_uv, w_fold)
+    o_lat = torch.empty(B, s_q, H, w.latent, dtype=torch.float32, device="cuda")
+    _fill(o_lat, gen)
+    out = torch.empty(B, s_q, H, w.v, dtype=dt, device="cuda")
+    y = torch.empty(B, s_q, hidden, dtype=dt, device="cuda")
+    rows = []
+    wo_bytes, wf_bytes = w_o.numel() * 2.0, w_fold.numel() * 2.0
+    uv_bytes = w_uv.numel() * 2.0
+    cases = (
+        ("W_O", lambda: L.gqla_out_hidden(d, hidden, False, out, w_o, y), wo_bytes),
+        ("W_UV then W_O", lambda: (L.gqla_out_proj(d, o_lat, w_uv, out), L.gqla_out_hidden(d, hidden, False, out, w_o, y)),
+         wo_bytes + uv_bytes),
+        ("W_O with W_UV folded", lambda: L.gqla_out_hidden(d, hidden, True, o_lat, w_fold, y), wf_bytes),
+    )
+    for label, fn, nbytes in cases:
+        t_med, t_best = _time(fn, reps, flush)
+        r = {"workload": name, "path": "output side", "op": label, "s_q": s_q, "batch": B, "hidden": hidden,
+             "ms": t_med * 1e3, "best_ms": t_best * 1e3, "weight_bytes": nbytes, "weight_GBps": nbytes / t_med / 1e9,
+             "hbm_frac": nbytes / t_med / HBM_PEAK}
+        rows.append(r)
+        print(json.dumps(r), flush=True)
+    del w_o, w_uv, w_fold, o_lat, out, y
+    torch.cuda.empty_cache()
+    return rows
+
+
 def table(rows):
     out = ["| workload | path | s_q | batch | ms (median) | best ms | tokens/s | KV GB/s | % HBM | TFLOP/s | % MFMA | bound | splits |",
            "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for r in rows:
-        if r["path"] == "append":
+        if r["path"] in ("append", "output side"):
             continue
         out.append(f"| {r['workload']} | {r['path']} | {r['s_q']} | {r['batch']} | {r['ms']:.3f} | {r['best_ms']:.3f} | "
                    f"{r['tokens_per_s']:,.0f} | {r['kv_GBps']:,.0f} | {r['hbm_frac'] * 100:.1f} | {r['tflops']:.0f} | "
@@ -217,6 +263,12 @@ def table(rows):
     if app:
         out += ["", "| workload | append: tokens | ms (median) | us per token |", "|---|---|---|---|"]
         out += [f"| {r['workload']} | {r['tokens']} | {r['ms']:.4f} | {r['us_per_token']:.3f} |" for r in app]
+    osd = [r for r in rows if r["path"] == "output side"]
+    if osd:
+        out += ["", "| workload | output side (s_q = 1) | rows | hidden | ms (median) | weight GB/s | % HBM |",
+                "|---|---|---|---|---|---|---|"]
+        out += [f"| {r['workload']} | {r['op']} | {r['batch'] * r['s_q']} | {r['hidden']} | {r['ms']:.4f} | "
+                f"{r['weight_GBps']:,.0f} | {r['hbm_frac'] * 100:.1f} |" for r in osd]
     return "\n".join(out)
 
 
@@ -224,15 +276,20 @@ def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--workloads", default=",".join(CASES))
     ap.add_argument("--reps", type=int, default=10)
+    ap.add_argument("--output-side", default="llama3-8b-b32-ctx8k,dsv3-b64-ctx8k",
+                    help="workloads whose output side (W_O, folded or not) is timed; empty for none")
     ap.add_argument("--out", default=None)
     a = ap.parse_args(argv)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(2025)
     flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
     rows = []
-    for name in a.workloads.split(","):
+    for name in filter(None, a.workloads.split(",")):
         print(f"[sweep] {name}", file=sys.stderr, flush=True)
         rows += run_workload(name, a.reps, gen, flush)
+    for name in filter(None, a.output_side.split(",")):
+        print(f"[sweep] output side {name}", file=sys.stderr, flush=True)
+        rows += run_output_side(name, a.reps, gen, flush)
     t = table(rows)
     print(t)
     if a.out:

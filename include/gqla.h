@@ -204,6 +204,37 @@ gqla_status gqla_append_tokens(const gqla_dims* dims, const gqla_paged* paged, c
                                const void* kr_new, float rope_theta, const void* w_uk, const void* w_uv,
                                void* latent_cache, void* expanded_cache, void* stream);
 
+/*
+ * Output side: the layer's output projection W_O after the heads (gqla_attn.py module
+ * source, GQLAAttention: a bias-free out_proj from H*head_dim to hidden_size applied to
+ * the heads' outputs laid side by side head-major), on either path.
+ *
+ * gqla_out_hidden — y = x W^T over the B*s_q rows of the batch:
+ *   folded = 0: x = the heads' outputs, data [B][s_q][H][d_v] (gqla_out_proj or
+ *               gqla_decode_gqa output), w = W_O, data [hidden][H*d_v]:
+ *               y[r][n] = sum_{h,v} W_O[n][h*d_v + v] x[r][h][v];
+ *   folded = 1: x = the absorb path's latent outputs, fp32 [B][s_q][H][d_c]
+ *               (gqla_decode_absorb output, no gqla_out_proj), w = W_fold from
+ *               gqla_fold_out_weight, data [hidden][H*d_c]:
+ *               y[r][n] = sum_{h,c} W_fold[n][h*d_c + c] x[r][h][c];
+ *   y : data [B][s_q][hidden] (output; fp32 accumulation, rounded once to the data type).
+ * Both give the same y up to rounding. hidden is free (the configurations fix none; the
+ * module ties it to H * head_dim). The fold reads d_c / d_v times more weight bytes per
+ * step than W_O plus W_UV, so at decode batch sizes it is the slower form on MI355X.
+ * Errors: GQLA_ERR_INVALID_ARG for bad dims, hidden outside [1, 65535] or NULL pointers.
+ */
+gqla_status gqla_out_hidden(const gqla_dims* dims, int32_t hidden, int32_t folded, const void* x,
+                            const void* w, void* y, void* stream);
+
+/*
+ * gqla_fold_out_weight — W_O with every head's W_UV^g folded in (once per model):
+ *   W_fold[n][h*d_c + c] = sum_v W_O[n][h*d_v + v] W_UV^g[v][c],  g = h / gs.
+ *   w_o : data [hidden][H*d_v];  w_uv : data [G][d_v][d_c];  w_fold : data [hidden][H*d_c]
+ * (fp32 accumulation, rounded once to the data type). Errors as gqla_out_hidden.
+ */
+gqla_status gqla_fold_out_weight(const gqla_dims* dims, int32_t hidden, const void* w_o, const void* w_uv,
+                                 void* w_fold, void* stream);
+
 /* Number of KV splits the decode call for `path` will use (host arithmetic only). */
 gqla_status gqla_num_splits(const gqla_dims* dims, const gqla_paged* paged, int32_t path,
                             int32_t* n);
