@@ -21,7 +21,7 @@ namespace gqla {
 // bench.py and the crossover sweep; see the path-crossover profile).
 struct Mi355xRates {
   double absorb_bw = 5.0e12;      // absorb decode latent streaming, B/s (tile copies into LDS)
-  double absorb_mfma = 0.65e15;   // absorb decode when MFMA/LDS-bound, flop/s
+  double absorb_mfma = 0.8e15;    // absorb decode when MFMA/LDS-bound, flop/s
   double gqa_bw = 6.4e12;         // GQA decode expanded-cache streaming, B/s (per-group layout)
   double gqa_shared_bw = 6.3e12;  // same, RoPE key once per block
   double gqa_mfma = 1.0e15;       // GQA decode padded MFMA work, flop/s
