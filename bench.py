@@ -1,7 +1,9 @@
 """Decode-attention benchmark of the GQLA hot path on one MI355X.
 
 One step = one pass of the whole hot path over one batch of synthetic, seeded input:
-  1. gqla_expand_cache of the blocks that hold each sequence's s_q new tokens,
+  1. gqla_append_tokens of each sequence's s_q = 2 new tokens: their latent rows with the
+     key rotated to its position, and their expansion into every group's K/V (the
+     expansion the GQA path needs, for exactly the tokens that are new),
   2. MQA-absorb path at s_q = 1: gqla_absorb_query -> gqla_decode_absorb -> gqla_out_proj,
   3. GQA path at s_q = 2:        gqla_decode_gqa over the expanded cache.
 `value` = decode tokens produced per second by the step (B*1 absorb + B*2 GQA tokens).
@@ -188,13 +190,12 @@ def main():
     expanded = torch.empty(x.num_blocks * per_block, dtype=torch.bfloat16, device="cuda")
     all_ids = torch.arange(x.num_blocks, dtype=torch.int32, device="cuda")
     G.gqla_expand_cache(d_gqa, cache, w_uk, w_uv, all_ids, x.num_blocks, expanded)
-    # blocks holding the s_q newest tokens of every sequence (re-expanded each step)
-    tail = set()
-    for b in range(B):
-        L = int(x.ctx_lens[b])
-        for t in range(L - a.gqa_sq, L):
-            tail.add(int(x.block_table[b, t // 64]))
-    tail_ids = torch.tensor(sorted(tail), dtype=torch.int32, device="cuda")
+    # the s_q newest tokens of every sequence: seeded N(0, 1) latent rows and (unrotated)
+    # RoPE keys, appended at positions L - s_q .. L - 1 every step (the same values each time)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed + 77)
+    c_app = torch.randn(B, a.gqa_sq, w.latent, generator=gen, device="cuda").to(torch.bfloat16)
+    kr_app = torch.randn(B, a.gqa_sq, w.rope, generator=gen, device="cuda").to(torch.bfloat16)
 
     q_abs = torch.empty(B, a.absorb_sq, H, w.latent + w.rope, dtype=torch.bfloat16, device="cuda")
     o_lat = torch.empty(B, a.absorb_sq, H, w.latent, dtype=torch.float32, device="cuda")
@@ -209,7 +210,7 @@ def main():
     def step(record):
         ev = [E() for _ in range(4)] if record else None
         if record: ev[0].record()
-        G.gqla_expand_cache(d_gqa, cache, w_uk, w_uv, tail_ids, x.num_blocks, expanded)
+        G.gqla_append_tokens(d_gqa, paged, c_app, kr_app, 10000.0, w_uk, w_uv, cache, expanded)
         if record: ev[1].record()
         G.gqla_absorb_query(d_abs, q_nope1, q_rope1, w_uk, q_abs)
         G.gqla_decode_absorb(d_abs, paged, q_abs, cache, ws_abs, o_lat)
@@ -246,20 +247,7 @@ def main():
     t_exp = np.mean([m[0].elapsed_time(m[1]) for m in marks])
     t_abs = np.mean([m[1].elapsed_time(m[2]) for m in marks])
     t_gqa = np.mean([m[2].elapsed_time(m[3]) for m in marks])
-    log(f"[bench] ms/step {ms_step:.4f}: expand {t_exp:.4f} absorb {t_abs:.4f} gqa {t_gqa:.4f}")
-
-    # The append path (not part of the step): the s_q GQA-path tokens of every sequence
-    # written into the latent cache with their rotated keys and expanded into the groups.
-    c_app = torch.randn(B, a.gqa_sq, w.latent, device="cuda").to(torch.bfloat16)
-    kr_app = torch.randn(B, a.gqa_sq, w.rope, device="cuda").to(torch.bfloat16)
-    G.gqla_append_tokens(d_gqa, paged, c_app, kr_app, 10000.0, w_uk, w_uv, cache, expanded)
-    e0, e1 = E(), E()
-    e0.record()
-    for _ in range(a.steps):
-        G.gqla_append_tokens(d_gqa, paged, c_app, kr_app, 10000.0, w_uk, w_uv, cache, expanded)
-    e1.record()
-    torch.cuda.synchronize()
-    t_app = e0.elapsed_time(e1) / a.steps
+    log(f"[bench] ms/step {ms_step:.4f}: append {t_exp:.4f} absorb {t_abs:.4f} gqa {t_gqa:.4f}")
 
     ctx = x.ctx_lens.astype(np.int64)
     elt = 2
@@ -291,8 +279,8 @@ def main():
                     "kv_bytes": kv_gqa, "kv_GBps": kv_gqa / (t_gqa / 1e3) / 1e9,
                     "hbm_frac": kv_gqa / (t_gqa / 1e3) / 1e9 / HBM_PEAK_GBS,
                     "flops": fl_gqa, "mfma_frac": fl_gqa / (t_gqa / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
-            "expand_tail": {"blocks": int(tail_ids.numel()), "ms": t_exp},
-            "append": {"tokens": B * a.gqa_sq, "ms": t_app, "note": "gqla_append_tokens with expansion, timed apart from the step"},
+            "append": {"tokens": B * a.gqa_sq, "ms": t_exp,
+                       "note": "gqla_append_tokens: new latent rows, RoPE, expansion into the groups"},
         },
         "roofline": {"kernel": "gqa_decode_split (gqla_decode_gqa)", "bound": "hbm",
                      "achieved": kv_gqa / (t_gqa / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
