@@ -361,7 +361,8 @@ bool tuned_gqa_supported(const gqla_dims* d) {
 }
 
 // One 4-wave workgroup per CU per round: on MI355X the unsplit launch streams fastest
-// (5.8 TB/s on the LLaMA-3-8B shape, against 4.6 TB/s with four splits and a combine),
+// (LLaMA-3-8B batch 32 s_q = 2, shared RoPE key: 129 us unsplit against 139 / 153 us with
+// two / four splits and a combine),
 // so the context is only split when sequences x groups cannot cover the CUs.
 int tuned_gqa_target_wgs() { return kNumCUs; }
 int tuned_gqa_min_blocks_per_split() { return 8; }
