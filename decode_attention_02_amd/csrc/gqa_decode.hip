@@ -68,7 +68,7 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_split(AttnParams p) {
   constexpr int KSN = SHARED ? (DQK - 64) / 32 : KS;   // k-steps held in the group chunk
   constexpr int KF = 32 * KSN;     // K features in the group chunk
   constexpr int NT = DV / 16;      // feature tiles of the value product
-  constexpr bool kHalfUnits = RT == 2 && DQK > 128;
+  constexpr bool kHalfUnits = (RT == 2 && DQK > 128) || kWaves == 8;
   __shared__ float s_o[kWaves][RT][NT][64][4];   // per-wave O^T fragments (lane-major)
   __shared__ float s_m[kWaves][RT * 16];
   __shared__ float s_l[kWaves][RT * 16];
@@ -266,8 +266,9 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_split(AttnParams p) {
       }
     }
   } else {
-    // Register budget of two row tiles at d_qk = 192: two half blocks in flight instead
-    // (the next half's loads issued before the current half is consumed).
+    // Two half blocks in flight (the next half's loads issued before the current half is
+    // consumed): the register budget of two row tiles at d_qk = 192, and of two waves per
+    // SIMD in the 8-wave workgroups.
     if (n_my > 0) {
       const int nu = 2 * n_my;
       auto unit_chunk = [&](int u) { return chunk_of(block_id(min(u, nu - 1) >> 1)); };
@@ -360,16 +361,20 @@ bool tuned_gqa_supported(const gqla_dims* d) {
          (d->rope_shared == 0 || d->rope_dim == 64);
 }
 
-// One 4-wave workgroup per CU per round: on MI355X the unsplit launch streams fastest
+// One workgroup per CU per round: on MI355X the unsplit launch streams fastest
 // (LLaMA-3-8B batch 32 s_q = 2, shared RoPE key: 129 us unsplit against 139 / 153 us with
 // two / four splits and a combine),
 // so the context is only split when sequences x groups cannot cover the CUs.
 int tuned_gqa_target_wgs() { return kNumCUs; }
 int tuned_gqa_min_blocks_per_split() { return 8; }
 
+// One row tile: 8 waves (two per SIMD, half a block in flight each), which keeps the same
+// bytes in flight as 4 waves with two blocks each but lets one wave's loads run while the
+// other does its softmax (4.5% faster on the long-context batch, equal on LLaMA-3-8B).
+// Two row tiles need the registers of one wave per SIMD.
 template <int DQK, int RT, bool SHARED>
 hipError_t launch_dqk(const AttnParams& p, hipStream_t s) {
-  constexpr int kWaves = 4;
+  constexpr int kWaves = RT == 1 ? 8 : 4;
   const int64_t units = static_cast<int64_t>(p.B) * p.n_split;
   const int64_t wgs = SHARED ? (units + 7) / 8 * 8 * p.kv_heads : units * p.kv_heads;
   if (wgs > 0x7fffffff) return hipErrorInvalidConfiguration;
