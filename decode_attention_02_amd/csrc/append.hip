@@ -149,15 +149,16 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // bf16 with d_c % 32 == 0 and (d_n + d_v) % 16 == 0: the projections on MFMA. Workgroup
-// (token tile, group, z) has 4 waves, wave w taking the 16 stacked weight rows
+// (token tile, group, z < nz) has 4 waves, wave w taking the 16 stacked weight rows
 // 16 * (4z + w) .. +16 of [W_UK^g ; W_UV^g]: K^T/V^T = W C^T with A = 16 weight rows x 32
 // latent values and B = 32 latent values x 16 tokens, both read straight from global
-// memory with every load of the wave in flight at once. The z = 0 workgroups also rotate
-// the tile's keys, write the latent rows (group 0) and copy the keys into K.
+// memory with every load of the wave in flight at once. The workgroups z = nz rotate the
+// tile's keys, write the latent rows (group 0) and copy the keys into K, so that neither
+// kind waits for the other's memory round trips (the step is latency-bound).
 template <int DC>
 __global__ __launch_bounds__(256) void append_tokens_mfma(AppendParams a, const bf16_t* c_new, const bf16_t* kr_new,
                                                           const bf16_t* w_uk, const bf16_t* w_uv, bf16_t* latent,
-                                                          bf16_t* expanded) {
+                                                          bf16_t* expanded, int nz) {
   constexpr int KS = DC / 32;
   const int dq = DC + a.dr;
   const ExpandedLayout lay = expanded_layout(a.dn, a.dr, a.dv, a.G, a.rope_shared != 0);
@@ -183,7 +184,7 @@ __global__ __launch_bounds__(256) void append_tokens_mfma(AppendParams a, const 
   const int rows = a.dn + a.dv;
   const int row0 = 16 * (4 * blockIdx.z + wave);
   // Issue every operand load of this wave first.
-  const bool live_rows = row0 < rows;
+  const bool live_rows = static_cast<int>(blockIdx.z) < nz && row0 < rows;
   bf16x8 wa[KS], cb[KS];
   if (live_rows) {
     const int r = row0 + col;
@@ -198,8 +199,19 @@ __global__ __launch_bounds__(256) void append_tokens_mfma(AppendParams a, const 
     }
   }
   __syncthreads();   // s_dst
-  if (blockIdx.z == 0) {
-    // Rotated keys of the tile (fp64 angle, rounded once), the latent rows, K's RoPE part.
+  if (static_cast<int>(blockIdx.z) == nz) {
+    if (a.rope_shared && g != 0) return;   // the shared key and the latent rows are group 0's
+    // The latent rows (group 0), then the rotated keys of the tile (fp64 angle, rounded
+    // once) into the latent rows and K's RoPE part.
+    if (g == 0) {
+      for (int idx = threadIdx.x; idx < kAppendTile * (DC / 8); idx += blockDim.x) {
+        const int j = idx / (DC / 8), c8 = idx % (DC / 8);
+        const int64_t dst = s_dst[j];
+        if (dst < 0) continue;
+        *reinterpret_cast<uint4*>(latent + dst * dq + 8 * c8) =
+            *reinterpret_cast<const uint4*>(c_new + static_cast<int64_t>(n0 + j) * DC + 8 * c8);
+      }
+    }
     __shared__ bf16_t s_rope[kAppendTile * 128];
     const int half = a.dr / 2;
     for (int idx = threadIdx.x; idx < kAppendTile * a.dr; idx += blockDim.x) {
@@ -228,15 +240,6 @@ __global__ __launch_bounds__(256) void append_tokens_mfma(AppendParams a, const 
         blk[static_cast<int64_t>(sl) * kBlock * kSlab + s * w + k % kSlab] = s_rope[idx];
       }
       if (g == 0) latent[dst * dq + DC + k] = s_rope[idx];
-    }
-    if (g == 0) {
-      for (int idx = threadIdx.x; idx < kAppendTile * (DC / 8); idx += blockDim.x) {
-        const int j = idx / (DC / 8), c8 = idx % (DC / 8);
-        const int64_t dst = s_dst[j];
-        if (dst < 0) continue;
-        *reinterpret_cast<uint4*>(latent + dst * dq + 8 * c8) =
-            *reinterpret_cast<const uint4*>(c_new + static_cast<int64_t>(n0 + j) * DC + 8 * c8);
-      }
     }
   }
   if (!live_rows) return;
@@ -270,10 +273,11 @@ hipError_t launch_append(const AppendParams& a, const void* c_new, const void* k
                          const void* w_uv, void* latent, void* expanded, bool bf16, hipStream_t s) {
   const int tiles = (a.n_tok + kAppendTile - 1) / kAppendTile;
   if (bf16 && expanded != nullptr && a.dc == 512 && a.dr <= 128 && (a.dn + a.dv) % 16 == 0) {
-    dim3 grid(tiles, a.G, (a.dn + a.dv + 63) / 64);
+    const int nz = (a.dn + a.dv + 63) / 64;
+    dim3 grid(tiles, a.G, nz + 1);
     append_tokens_mfma<512><<<grid, 256, 0, s>>>(a, static_cast<const bf16_t*>(c_new), static_cast<const bf16_t*>(kr_new),
                                                  static_cast<const bf16_t*>(w_uk), static_cast<const bf16_t*>(w_uv),
-                                                 static_cast<bf16_t*>(latent), static_cast<bf16_t*>(expanded));
+                                                 static_cast<bf16_t*>(latent), static_cast<bf16_t*>(expanded), nz);
     return hipGetLastError();
   }
   dim3 grid(tiles, expanded != nullptr ? a.G : 1);

@@ -168,6 +168,44 @@ hipError_t launch_generic_attn(const AttnParams& p, bool bf16, hipStream_t s) {
 __global__ __launch_bounds__(128) void combine_splits(CombineParams c) {
   const int64_t row = blockIdx.x;
   const float* lse = c.ws_lse + row * c.n_split;
+  constexpr int kFew = 8;
+  if ((c.dvo & 3) == 0 && c.n_split <= kFew) {
+    // Up to 8 splits: the split lse values and the partial outputs load together (one
+    // memory round trip per row instead of two).
+    float l[kFew];
+#pragma unroll
+    for (int s = 0; s < kFew; ++s) l[s] = s < c.n_split ? lse[s] : -INFINITY;
+    const float* o = c.ws_o + row * c.n_split * c.dvo;
+    for (int f = 4 * threadIdx.x; f < c.dvo; f += 4 * blockDim.x) {
+      float4 v[kFew];
+#pragma unroll
+      for (int s = 0; s < kFew; ++s)
+        if (s < c.n_split) v[s] = *reinterpret_cast<const float4*>(o + static_cast<int64_t>(s) * c.dvo + f);
+      float m = -INFINITY;
+      bool has_nan = false;
+#pragma unroll
+      for (int s = 0; s < kFew; ++s) {
+        has_nan |= l[s] != l[s];
+        m = fmaxf(m, l[s]);
+      }
+      float tot = 0.f;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int s = 0; s < kFew; ++s) {
+        if (s < c.n_split && l[s] != -INFINITY) {
+          const float w = expf(l[s] - m);
+          tot += w;
+          acc.x += w * v[s].x; acc.y += w * v[s].y; acc.z += w * v[s].z; acc.w += w * v[s].w;
+        }
+      }
+      const bool nan_row = has_nan || !(tot > 0.f);
+      const float inv = 1.f / tot;
+      const float r[4] = {acc.x, acc.y, acc.z, acc.w};
+      for (int k = 0; k < 4; ++k) store_out(c.out, c.out_kind, row * c.dvo + f + k, nan_row ? nan_f32() : r[k] * inv);
+      if (c.lse != nullptr && f == 0) c.lse[row] = nan_row ? nan_f32() : m + logf(tot);
+    }
+    return;
+  }
   float m = -INFINITY;
   bool has_nan = false;
   for (int s = 0; s < c.n_split; ++s) {
