@@ -15,9 +15,12 @@
 //     workgroup copies a [d_n][128] column slice of W_UK^g into LDS (global_load_lds)
 //     and reads the weight operand transposed with ds_read_b64_tr_b16;
 //   * value output: out^T = W_UV^g o_lat^T contracts over W_UV's contiguous column
-//     index, so each wave keeps its 32 rows of W_UV^g in registers (direct 16-byte loads)
-//     across the row tiles it visits. The fp32 latent output is split into bf16 high and
-//     low parts (two MFMAs) so the product keeps close to fp32 accuracy.
+//     index, so each single-wave workgroup keeps its 32 rows of W_UV^g in registers
+//     (direct 16-byte loads) across the row tiles it visits. The fp32 latent output is
+//     split into bf16 high and low parts (two MFMAs) so the product keeps close to fp32
+//     accuracy.
+// Workgroups are small (one wave; four for the absorbed query at large row counts) so the
+// weight and row reads of a small batch spread over most CUs instead of a few.
 #include "device_common.h"
 #include "gqla_internal.h"
 #include "tuned.h"
@@ -50,15 +53,18 @@ __device__ __forceinline__ int64_t group_row(int rg, int g, int gs, int H) {
 // gives those rows distinct chunk pairs, so a 32-lane read covers all 64 banks once.
 __device__ __forceinline__ int swz(int r) { return 2 * ((r & 3) | (((r >> 3) & 1) << 2)); }
 
-template <int DN>
-__global__ __launch_bounds__(256) void absorb_query_kernel(ProjParams d, const bf16_t* q_nope, const bf16_t* q_rope,
-                                                           const bf16_t* w_uk, bf16_t* q_abs) {
+// NW waves per workgroup, 16 rows each: 4 when the rows are many (the staged weight slice
+// serves 64 rows), 1 when 64-row workgroups would leave most CUs idle.
+template <int DN, int NW>
+__global__ __launch_bounds__(NW * 64) void absorb_query_kernel(ProjParams d, const bf16_t* q_nope, const bf16_t* q_rope,
+                                                               const bf16_t* w_uk, bf16_t* q_abs) {
   __shared__ __attribute__((aligned(16))) char w[DN * kSliceF * 2];
+  constexpr int RW = 16 * NW;   // rows per workgroup pass
   const int g = blockIdx.z;
   const int f0 = blockIdx.x * kSliceF;
   const int gs = d.H / d.G;
   const int rows_g = d.rows * gs;
-  const int n_rt = (rows_g + 63) / 64;
+  const int n_rt = (rows_g + RW - 1) / RW;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
   constexpr int KS = DN / 32;
@@ -67,7 +73,7 @@ __global__ __launch_bounds__(256) void absorb_query_kernel(ProjParams d, const b
   {
     const bf16_t* src = w_uk + static_cast<int64_t>(g) * DN * kDC + f0;
 #pragma unroll
-    for (int i = wave; i < DN / 4; i += 4) {
+    for (int i = wave; i < DN / 4; i += NW) {
       const int r = 4 * i + (lane >> 4);
       const int c = (lane & 15) ^ swz(r);
       __builtin_amdgcn_global_load_lds(src + r * kDC + 8 * c, (lds_void*)(w + 1024 * i), 16, 0, 0);
@@ -81,7 +87,7 @@ __global__ __launch_bounds__(256) void absorb_query_kernel(ProjParams d, const b
   const int src_b = 8 * (col & 3);   // byte offset inside the 32-byte feature tile
   bool staged = false;
   for (int rt = blockIdx.y; rt < n_rt; rt += gridDim.y) {
-    const int rg = rt * 64 + wave * 16 + col;   // this lane's row (B operand column)
+    const int rg = rt * RW + wave * 16 + col;   // this lane's row (B operand column)
     const bool live = rg < rows_g;
     const int64_t row = group_row(live ? rg : rows_g - 1, g, gs, d.H);   // past the end: re-read the last row
     bf16x8 qf[KS];
@@ -116,8 +122,8 @@ __global__ __launch_bounds__(256) void absorb_query_kernel(ProjParams d, const b
     // The RoPE part is a copy (64 values = 8 chunks of 16 bytes per row), done by the
     // first feature slice.
     if (blockIdx.x == 0) {
-      for (int i = threadIdx.x; i < 64 * (kDR / 8); i += blockDim.x) {
-        const int r = rt * 64 + i / (kDR / 8), c = i % (kDR / 8);
+      for (int i = threadIdx.x; i < RW * (kDR / 8); i += blockDim.x) {
+        const int r = rt * RW + i / (kDR / 8), c = i % (kDR / 8);
         if (r >= rows_g) continue;
         const int64_t rr = group_row(r, g, gs, d.H);
         *reinterpret_cast<uint4*>(q_abs + rr * dq + kDC + 8 * c) =
@@ -127,12 +133,12 @@ __global__ __launch_bounds__(256) void absorb_query_kernel(ProjParams d, const b
   }
 }
 
-__global__ __launch_bounds__(256) void out_proj_kernel(ProjParams d, const float* o_lat, const bf16_t* w_uv, bf16_t* out) {
+__global__ __launch_bounds__(64) void out_proj_kernel(ProjParams d, const float* o_lat, const bf16_t* w_uv, bf16_t* out) {
   const int g = blockIdx.y;
   const int gs = d.H / d.G;
   const int rows_g = d.rows * gs;
   const int n_rt = (rows_g + 15) / 16;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x, wave = blockIdx.z;   // one wave per workgroup: its 32 rows of W_UV^g
   const int col = lane & 15, grp = lane >> 4;
   // A operand, kept for every row tile: W_UV^g rows 32*wave + 16*t + col, latent values
   // 32*ks + 8*grp .. +8.
@@ -201,15 +207,21 @@ bool tuned_absorb_query_supported(const gqla_dims* d) {
 hipError_t launch_tuned_absorb_query(const ProjParams& p, const void* q_nope, const void* q_rope, const void* w_uk,
                                      void* q_abs, hipStream_t s) {
   const int rows_g = p.rows * (p.H / p.G);
-  const int n_rt = (rows_g + 63) / 64;
   const int per_row = (kDC / kSliceF) * p.G;
+  const bool wide = static_cast<int64_t>((rows_g + 63) / 64) * per_row >= kNumCUs;
+  const int n_rt = wide ? (rows_g + 63) / 64 : (rows_g + 15) / 16;
   dim3 grid(kDC / kSliceF, std::max(1, std::min(n_rt, kMaxWGs / per_row)), p.G);
   const bf16_t* qn = static_cast<const bf16_t*>(q_nope);
   const bf16_t* qr = static_cast<const bf16_t*>(q_rope);
   const bf16_t* wk = static_cast<const bf16_t*>(w_uk);
   bf16_t* qa = static_cast<bf16_t*>(q_abs);
-  if (p.dn == 128) absorb_query_kernel<128><<<grid, 256, 0, s>>>(p, qn, qr, wk, qa);
-  else absorb_query_kernel<64><<<grid, 256, 0, s>>>(p, qn, qr, wk, qa);
+  if (wide) {
+    if (p.dn == 128) absorb_query_kernel<128, 4><<<grid, 256, 0, s>>>(p, qn, qr, wk, qa);
+    else absorb_query_kernel<64, 4><<<grid, 256, 0, s>>>(p, qn, qr, wk, qa);
+  } else {
+    if (p.dn == 128) absorb_query_kernel<128, 1><<<grid, 64, 0, s>>>(p, qn, qr, wk, qa);
+    else absorb_query_kernel<64, 1><<<grid, 64, 0, s>>>(p, qn, qr, wk, qa);
+  }
   return hipGetLastError();
 }
 
@@ -220,11 +232,13 @@ bool tuned_out_proj_supported(const gqla_dims* d) {
 hipError_t launch_tuned_out_proj(const ProjParams& p, const float* o_lat, const void* w_uv, void* out, hipStream_t s) {
   const int rows_g = p.rows * (p.H / p.G);
   const int n_rt = (rows_g + 15) / 16;
-  // Each wave loads its 32 KiB of W_UV^g once; with many row tiles a wave visits at
-  // least 4 of them so that weight reloads stay small next to the latent-output reads.
+  // One wave per workgroup (32 rows of W_UV^g, z = which 32), so that the weight and
+  // latent-output reads spread over many CUs. Each wave loads its 32 KiB of W_UV^g once;
+  // with many row tiles a wave visits at least 4 of them so that weight reloads stay small
+  // next to the latent-output reads.
   const int want = std::max((n_rt + 3) / 4, 256 / p.G);
-  dim3 grid(std::max(1, std::min({n_rt, want, kMaxWGs / p.G})), p.G);
-  out_proj_kernel<<<grid, 256, 0, s>>>(p, o_lat, static_cast<const bf16_t*>(w_uv), static_cast<bf16_t*>(out));
+  dim3 grid(std::max(1, std::min({n_rt, want, kMaxWGs / p.G})), p.G, kDV / 32);
+  out_proj_kernel<<<grid, 64, 0, s>>>(p, o_lat, static_cast<const bf16_t*>(w_uv), static_cast<bf16_t*>(out));
   return hipGetLastError();
 }
 
