@@ -114,6 +114,31 @@ def test_absorb_path_matches_oracle(name, s_q, num_splits):
         assert le <= TOL["bf16"] * max(1.0, float(np.max(np.abs(r["lse"]))))
 
 
+@pytest.mark.parametrize("name,s_q,rope_shared", [("llama3-8b-b32-ctx8k", 1, True), ("dsv3-b64-ctx8k", 2, False)])
+def test_many_splits_match_oracle(name, s_q, rope_shared):
+    """16 one-block splits, so the split combine merges more than 8 partials per row (its
+    general loop rather than the all-loads-at-once form), on both paths."""
+    w = workload(name)
+    x = generate(w, s_q, batch=3, ctx_lens=[s_q, 700, 1000], shuffled=True, extra_blocks=2)
+    run = Run(x, 16, rope_shared)
+    G = run.G
+    for path in (G.GQLA_PATH_ABSORB, G.GQLA_PATH_GQA):
+        assert G.gqla_num_splits(run.dims, path, run.table.shape[1], run.paged.max_ctx_len,
+                                 x.num_blocks, 16) == 16
+    log(f"many splits {name} s_q={s_q} rope_shared={rope_shared}")
+    ga, gg = run.absorb(), run.gqa()
+    ref = oracle_paths(x)
+    for b in ref:
+        r = ref[b]
+        e = dict(o_lat=rel_err(ga["o_lat"][b], r["o_lat"]), absorb=rel_err(ga["out"][b], r["out"]),
+                 gqa=rel_err(gg["out"][b], r["out"]))
+        le = max(float(np.max(np.abs(ga["lse"][b] - r["lse"]))), float(np.max(np.abs(gg["lse"][b] - r["lse"]))))
+        log(f"  seq {b} L={int(x.ctx_lens[b])}: " + " ".join(f"{k} {v:.2e}" for k, v in e.items()) + f" lse_abs {le:.2e}")
+        for k, v in e.items():
+            assert v <= TOL["bf16"], (k, v)
+        assert le <= TOL["bf16"] * max(1.0, float(np.max(np.abs(r["lse"]))))
+
+
 def test_absorb_one_token_context_is_latent_row():
     """With one visible token the absorb decode returns that token's latent row exactly
     (fp32 o_lat of a bf16 value)."""
