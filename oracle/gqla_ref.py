@@ -34,7 +34,14 @@ Readings where the pages are silent (each also listed in the design notes):
   * with s_q new rows per sequence and a context of L tokens that includes them, row i
     sees tokens 0 .. L - s_q + i (bottom-right causal; the module masks with
     triu(diagonal=1) in decoder mode, which is this rule when the queries are the last
-    s_q positions).
+    s_q positions);
+  * RoPE rotates half-split pairs (component k with k + d_R/2) at angle
+    position * theta^(-2k/d_R), theta = 10000 (`rope_at`; the pages never describe RoPE);
+  * the output projection concatenates the heads' outputs head-major before W_O (the
+    module's transpose-then-view in forward(); `hidden_projection`);
+  * W_UV^g may be folded into W_O on the absorb path (`fold_out_weight`): both are linear
+    maps applied one after the other, so this is their product formed once; the pages
+    name the absorbed form but not this step.
 """
 import math
 from typing import List, Sequence, Tuple
