@@ -19,11 +19,16 @@ namespace gqla {
 
 // Effective throughputs of the kernels in this library, MI355X, bf16 (measured with
 // bench.py and the crossover sweep; see the path-crossover profile).
+// Each decode also has a fixed cost that does not shrink with the context: the first tile's
+// fetch before any compute, the partial-output stores, and the last workgroups' tail
+// (~15 us for the absorb decode by per-workgroup timestamps on LLaMA-3-8B batch 32).
 struct Mi355xRates {
-  double absorb_bw = 5.0e12;      // absorb decode latent streaming, B/s (tile copies into LDS)
+  double absorb_bw = 6.2e12;      // absorb decode latent streaming, B/s (tile copies into LDS)
   double absorb_mfma = 0.8e15;    // absorb decode when MFMA/LDS-bound, flop/s
-  double gqa_bw = 6.4e12;         // GQA decode expanded-cache streaming, B/s (per-group layout)
-  double gqa_shared_bw = 6.3e12;  // same, RoPE key once per block
+  double absorb_fixed_us = 15.0;  // absorb decode fixed cost
+  double gqa_bw = 6.8e12;         // GQA decode expanded-cache streaming, B/s (per-group layout)
+  double gqa_shared_bw = 6.6e12;  // same, RoPE key once per block
+  double gqa_fixed_us = 20.0;     // GQA step fixed cost (decode and new-token expansion)
   double gqa_mfma = 1.0e15;       // GQA decode padded MFMA work, flop/s
   double expand_mfma = 0.35e15;   // cache expansion, flop/s
   double proj_mfma = 0.2e15;      // absorbed-query and value projections, flop/s
@@ -46,7 +51,7 @@ PathEstimate estimate_paths(const gqla_dims* d, int64_t total_ctx, int n_split_a
   // MQA-absorb: absorbed query, latent decode, (combine), value projection.
   const double abs_bytes = tok * (dc + dr) * elt;
   const double abs_flops = vis * H * 2.0 * (2.0 * dc + dr);
-  double t_abs = std::max(us(abs_bytes / r.absorb_bw), us(abs_flops / r.absorb_mfma));
+  double t_abs = std::max(us(abs_bytes / r.absorb_bw), us(abs_flops / r.absorb_mfma)) + r.absorb_fixed_us;
   t_abs += 2 * r.launch_us + us(rows * dn * dc * 2.0 / r.proj_mfma) + us(rows * dc * dv * 4.0 / r.proj_mfma);
   if (n_split_abs > 1) t_abs += r.launch_us + us(rows * n_split_abs * dc * 4.0 / r.combine_bw);
 
@@ -55,7 +60,7 @@ PathEstimate estimate_paths(const gqla_dims* d, int64_t total_ctx, int n_split_a
   const double tile_rows = 16.0 * std::ceil(H / G * s / 16.0);
   const double gqa_flops = tok * G * tile_rows * 2.0 * (dqk + dv);
   const double gqa_bw = d->rope_shared ? r.gqa_shared_bw : r.gqa_bw;
-  double t_gqa = std::max(us(gqa_bytes / gqa_bw), us(gqa_flops / r.gqa_mfma));
+  double t_gqa = std::max(us(gqa_bytes / gqa_bw), us(gqa_flops / r.gqa_mfma)) + r.gqa_fixed_us;
   const double new_blocks = B * (1.0 + (s - 1.0) / kBlock);
   t_gqa += r.launch_us + us(new_blocks * G * kBlock * (dn + dv) * dc * 2.0 / r.expand_mfma);
   if (n_split_gqa > 1) t_gqa += r.launch_us + us(B * s * H * n_split_gqa * dv * 4.0 / r.combine_bw);
