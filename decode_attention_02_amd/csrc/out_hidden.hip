@@ -18,6 +18,8 @@
 #include "device_common.h"
 #include "gqla_internal.h"
 
+#include <type_traits>
+
 namespace gqla {
 namespace {
 
@@ -58,35 +60,38 @@ __global__ __launch_bounds__(kWaves * 64) void hidden_gemm(const void* x, const 
     for (int t = 0; t < MT; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // One chunk = U k-steps of the weight tiles and of the input rows, loaded together.
-  constexpr int U = XF32 ? 2 : kU;
+  // Two chunks must fit in registers beside the accumulators: a chunk holding more than
+  // 16 loads per lane would be parked in AGPRs, which waits for its loads at once.
+  constexpr int U = (XF32 || NTW * MT > 4) ? 2 : kU;
   constexpr int XV = XF32 ? 2 : 1;               // 16-byte loads per input operand
   struct Chunk {
     bf16x8 w[U][NTW];
     f32x4 x[U][MT][XV];                         // bf16 inputs use the bits of x[..][0]
   };
-  auto load = [&](Chunk& c, int s0) {
+  // Unconditional loads of chunk s0 .. s0 + U - 1 (always a whole chunk inside the range):
+  // no branch around a load, so every load of a chunk is in flight at once.
+  auto load = [&](Chunk& c, int s0, auto n) {
+    constexpr int NU = decltype(n)::value;   // k-steps to load (U, or 1 for the tail)
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bool ok = s0 + u < steps;
+    for (int u = 0; u < NU; ++u) {
 #pragma unroll
-      for (int j = 0; j < NTW; ++j)
-        c.w[u][j] = ok ? *reinterpret_cast<const bf16x8*>(wrow + j * wtile + 32 * (s0 + u)) : bf16x8{};
+      for (int j = 0; j < NTW; ++j) c.w[u][j] = *reinterpret_cast<const bf16x8*>(wrow + j * wtile + 32 * (s0 + u));
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
         if constexpr (XF32) {
           const float* xp = static_cast<const float*>(x) + xrow[t] + 32 * (s0 + u);
-          c.x[u][t][0] = ok ? *reinterpret_cast<const f32x4*>(xp) : f32x4{};
-          c.x[u][t][1] = ok ? *reinterpret_cast<const f32x4*>(xp + 4) : f32x4{};
+          c.x[u][t][0] = *reinterpret_cast<const f32x4*>(xp);
+          c.x[u][t][1] = *reinterpret_cast<const f32x4*>(xp + 4);
         } else {
-          const bf16_t* xp = static_cast<const bf16_t*>(x) + xrow[t] + 32 * (s0 + u);
-          c.x[u][t][0] = ok ? *reinterpret_cast<const f32x4*>(xp) : f32x4{};
+          c.x[u][t][0] = *reinterpret_cast<const f32x4*>(static_cast<const bf16_t*>(x) + xrow[t] + 32 * (s0 + u));
         }
       }
     }
   };
-  auto mma = [&](const Chunk& c) {
+  auto mma = [&](const Chunk& c, auto n) {
+    constexpr int NU = decltype(n)::value;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < NU; ++u) {
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
         if constexpr (XF32) {
@@ -112,15 +117,30 @@ __global__ __launch_bounds__(kWaves * 64) void hidden_gemm(const void* x, const 
     }
   };
 
-  // Two chunks in flight: the next chunk's loads go out before this one is used.
-  Chunk c0, c1;
-  load(c0, 0);
-  for (int s0 = 0; s0 < steps; s0 += 2 * U) {
-    load(c1, s0 + U);
-    mma(c0);
-    if (s0 + U >= steps) break;
-    load(c0, s0 + 2 * U);
-    mma(c1);
+  // Two chunks in flight: the next chunk's loads go out before this one is used. Whole
+  // chunks first (past the last one the last is loaded again, an L2 hit left unused), then
+  // the k-steps that do not fill a chunk one at a time.
+  const int nch = steps / U;
+  int ch = 0;
+  if (nch > 0) {
+    const std::integral_constant<int, U> whole;
+    Chunk ca, cb;
+    load(ca, 0, whole);
+    for (; ch + 1 < nch; ch += 2) {
+      load(cb, (ch + 1) * U, whole);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(ca, whole);
+      load(ca, min(ch + 2, nch - 1) * U, whole);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(cb, whole);
+    }
+    if (ch < nch) mma(ca, whole);
+  }
+  for (int s1 = nch * U; s1 < steps; ++s1) {
+    const std::integral_constant<int, 1> one;
+    Chunk c1;
+    load(c1, s1, one);
+    mma(c1, one);
   }
 
   // D[n][m]: lane holds features n0 + 16*j + 4*grp + r of row m0 + 16*t + col. Sum the
