@@ -13,8 +13,10 @@
 // contraction over its 4 waves; every wave streams its part of those rows with 16-byte
 // loads (the MFMA A operand straight from global memory, two chunks in flight) and reads
 // the rows' inputs, which every workgroup shares, from L2, each input operand feeding
-// one MFMA per weight tile. The 4 partial results are summed through LDS. An fp32 input is split into bf16 high and low parts (two MFMAs), which
-// keeps the product close to fp32 accuracy.
+// one MFMA per weight tile. The 4 partial results are summed through LDS. An fp32 input
+// is split into bf16 high and low parts (two MFMAs), which keeps the product close to fp32
+// accuracy. Wide layers with bf16 inputs (hidden >= 8192) use a second form that stages
+// both operands through LDS (hidden_dma below).
 #include "device_common.h"
 #include "gqla_internal.h"
 
@@ -199,6 +201,146 @@ hipError_t launch_x(const void* x, const void* w, void* y, int M, int N, int K, 
   return launch_ntw<XF32, 4>(x, w, y, M, N, K, s);
 }
 
+// bf16 inputs, 64 weight rows per workgroup: both operands stream through LDS. The
+// contraction is taken in 128-wide chunks; a chunk's stage holds the 64 weight rows and the
+// 16 * MT input rows (256 bytes each), copied global -> LDS with global_load_lds_dwordx4
+// (no registers held by a load in flight, whole 128-byte lines) three chunks ahead of its
+// use, in a ring of four stages. Wave w multiplies weight row tile w by every input row
+// tile over the whole contraction, so no partial sums need merging. In each 256-byte row
+// the 16-byte pieces are stored XOR-swizzled by the row index (piece p at p ^ (row % 16)),
+// so the 16 lanes that read one MFMA operand (16 rows, the same piece) hit distinct banks.
+constexpr int kDmaStages = 4;
+constexpr int kDmaStageBytes = 32 * 1024;   // 64 weight rows + up to 64 input rows, 256 B each
+__shared__ __attribute__((aligned(16))) char g_st0[kDmaStageBytes];
+__shared__ __attribute__((aligned(16))) char g_st1[kDmaStageBytes];
+__shared__ __attribute__((aligned(16))) char g_st2[kDmaStageBytes];
+__shared__ __attribute__((aligned(16))) char g_st3[kDmaStageBytes];
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int S>
+__device__ __forceinline__ char* stage_buf() {
+  return S == 0 ? g_st0 : S == 1 ? g_st1 : S == 2 ? g_st2 : g_st3;
+}
+
+template <int N>
+__device__ __forceinline__ void dma_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+}
+
+__device__ __forceinline__ void dma_barrier() {
+  // s_barrier without __syncthreads()'s fence, which would also wait for the copies that
+  // must stay in flight; callers wait for exactly the counters they need first.
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int MT>
+__global__ __launch_bounds__(256, 1) void hidden_dma(const bf16_t* x, const bf16_t* w, bf16_t* y, int M, int N, int K) {
+  constexpr int kRowsW = 64;
+  constexpr int kSlotsW = kRowsW * 16;               // 16-byte slots of the weight part
+  constexpr int kSlots = kSlotsW + 16 * MT * 16;     // plus the input part
+  constexpr int CPW = kSlots / 64 / 4;               // copies per wave per chunk (1 KiB each)
+  static_assert(CPW * 64 * 4 == kSlots && kSlots * 16 <= kDmaStageBytes, "stage layout");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int n0 = blockIdx.x * kRowsW;
+  const int m0 = blockIdx.y * 16 * MT;
+  const int nch = K / 128;
+  const char* wbase = reinterpret_cast<const char*>(w + static_cast<int64_t>(n0) * K);
+  const char* xbase = reinterpret_cast<const char*>(x + static_cast<int64_t>(m0) * K);
+  // Per-lane byte offsets (within a chunk's rows) of this wave's copies; input rows past M
+  // re-read row M - 1 (never stored).
+  uint32_t off[CPW];
+  bool is_w[CPW];
+#pragma unroll
+  for (int j = 0; j < CPW; ++j) {
+    const int slot = (wave * CPW + j) * 64 + lane;
+    is_w[j] = (wave * CPW + j) * 64 < kSlotsW;   // uniform per copy (parts are whole KiB)
+    const int part = is_w[j] ? slot : slot - kSlotsW;
+    const int row = part >> 4, piece = (part & 15) ^ (row & 15);
+    const int src_row = is_w[j] ? row : min(row, M - 1 - m0);
+    off[j] = static_cast<uint32_t>((static_cast<int64_t>(src_row) * K + 8 * piece) * 2);
+  }
+  auto issue = [&](int c, char* st) {
+    const int64_t kb = static_cast<int64_t>(min(c, nch - 1)) * 256;   // past the end: re-read the last chunk
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+      uint32_t o = off[j];
+      asm volatile("" : "+v"(o));   // a separate 32-bit operand, so the copy takes a scalar base
+      const char* src = (is_w[j] ? wbase : xbase) + kb;
+      __builtin_amdgcn_global_load_lds(src + o, (lds_void*)(st + (wave * CPW + j) * 1024), 16, 0, 2);
+    }
+  };
+  f32x4 acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Operand addresses inside a stage: weight row 16*wave + col, input row 16*t + col, piece
+  // 4*ks + grp of the chunk, swizzled by the row (row % 16 == col for both).
+  const int a_row = (16 * wave + col) * 256, b_row = kSlotsW * 16 + col * 256;
+  auto compute = [&](const char* st) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int pc = 16 * ((4 * ks + grp) ^ col);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(st + a_row + pc);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(st + b_row + t * 16 * 256 + pc);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[t], 0, 0, 0);
+      }
+    }
+  };
+  // Chunk c in stage c % 4: wait for its copies (c + 1 and c + 2 may stay in flight), pass
+  // the barrier that also frees stage (c + 3) % 4 (read in step c - 1), start chunk c + 3's
+  // copies into it, compute.
+  auto step = [&](int c, auto si) {
+    constexpr int S = decltype(si)::value;
+    dma_wait_vmcnt<2 * CPW>();
+    dma_barrier();
+    issue(c + 3, stage_buf<(S + 3) & 3>());
+    compute(stage_buf<S>());
+  };
+  issue(0, stage_buf<0>());
+  issue(1, stage_buf<1>());
+  issue(2, stage_buf<2>());
+  // Whole rounds of the ring, then the remaining 0-3 chunks (an exit inside an unrolled
+  // round would make the compiler's wait analysis drain every copy in flight).
+  const int nfull = nch & ~3;
+  int c = 0;
+  for (; c < nfull; c += 4) {
+    step(c, std::integral_constant<int, 0>());
+    step(c + 1, std::integral_constant<int, 1>());
+    step(c + 2, std::integral_constant<int, 2>());
+    step(c + 3, std::integral_constant<int, 3>());
+  }
+  if (c < nch) step(c, std::integral_constant<int, 0>());
+  if (c + 1 < nch) step(c + 1, std::integral_constant<int, 1>());
+  if (c + 2 < nch) step(c + 2, std::integral_constant<int, 2>());
+  dma_wait_vmcnt<0>();   // the copies past the end have landed before the workgroup ends
+  // D[n][m]: lane holds features n0 + 16*wave + 4*grp + r of input row m0 + 16*t + col.
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int m = m0 + 16 * t + col;
+    if (m < M) {
+      bf16_t packed[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) packed[r] = f32_to_bf16(acc[t][r]);
+      *reinterpret_cast<uint2*>(y + static_cast<int64_t>(m) * N + n0 + 16 * wave + 4 * grp) =
+          *reinterpret_cast<uint2*>(packed);
+    }
+  }
+}
+
+template <int MT>
+hipError_t launch_dma(const void* x, const void* w, void* y, int M, int N, int K, hipStream_t s) {
+  const dim3 grid(N / 64, (M + 16 * MT - 1) / (16 * MT));
+  hidden_dma<MT><<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(w),
+                                      static_cast<bf16_t*>(y), M, N, K);
+  return hipGetLastError();
+}
+
 // Generic: one thread per output, fp32 accumulation; any sizes, fp32 or bf16 data.
 template <typename T, typename TX>
 __global__ __launch_bounds__(256) void generic_hidden(const TX* x, const T* w, T* y, int M, int N, int K) {
@@ -232,6 +374,11 @@ __global__ __launch_bounds__(256) void fold_kernel(ProjParams d, int hidden, con
 hipError_t launch_out_hidden(const void* x, bool x_f32, const void* w, void* y, int M, int N, int K, bool bf16,
                              hipStream_t s) {
   if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
+  if (bf16 && !x_f32 && N % 64 == 0 && N / 64 >= kNumCUs / 2 && K % 128 == 0 && K <= (1 << 20)) {
+    if (M <= 16) return launch_dma<1>(x, w, y, M, N, K, s);
+    if (M <= 32) return launch_dma<2>(x, w, y, M, N, K, s);
+    return launch_dma<4>(x, w, y, M, N, K, s);
+  }
   if (bf16 && N % 16 == 0 && K % (32 * kWaves) == 0)
     return x_f32 ? launch_x<true>(x, w, y, M, N, K, s) : launch_x<false>(x, w, y, M, N, K, s);
   const int64_t n = static_cast<int64_t>(M) * N;

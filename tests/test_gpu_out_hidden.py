@@ -2,7 +2,8 @@
 oracle, on seeded host inputs: W_O over the heads' outputs, the fold of W_UV^g into W_O, and
 the folded projection over the absorb path's fp32 latent outputs. Row counts cover one row,
 a ragged last 16-row tile and several row passes; hidden sizes cover the module's
-H * head_dim, an untied size and one that is not a multiple of 16 (generic kernel)."""
+H * head_dim, untied sizes (both weight-streaming forms: per-wave register chunks, and 64-row
+LDS-staged chunks from hidden 8192 up) and one that is not a multiple of 16 (generic kernel)."""
 import zlib
 
 import numpy as np
@@ -46,6 +47,9 @@ def _dims(H, Gr, dc, dv, dtype, B, s_q):
     ("tiny-fp32", 256, 2, 2), ("tiny-fp32", 100, 3, 1),
     ("llama3-8b", 4096, 32, 1), ("llama3-8b", 4096, 3, 2), ("llama3-8b", 4096, 1, 1), ("llama3-8b", 4100, 5, 1),
     ("dsv3", 7168, 40, 2), ("dsv3", 16384, 2, 1),
+    # 64-row LDS-staged form (hidden a multiple of 64, >= 128 workgroups): 1, 2 and 4 row
+    # tiles, a ragged last tile, and two passes over the rows
+    ("dsv3", 16384, 64, 1), ("dsv3", 8192, 70, 1), ("llama3-8b", 8192, 20, 1), ("llama3-8b", 16384, 13, 1),
     ("dsv3-tp8share", 2048, 9, 2),
 ])
 def test_out_hidden_matches_oracle(name, hidden, B, s_q):
