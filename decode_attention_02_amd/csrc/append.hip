@@ -201,28 +201,42 @@ __global__ __launch_bounds__(256) void append_tokens_mfma(AppendParams a, const 
   __syncthreads();   // s_dst
   if (static_cast<int>(blockIdx.z) == nz) {
     if (a.rope_shared && g != 0) return;   // the shared key and the latent rows are group 0's
-    // The latent rows (group 0), then the rotated keys of the tile (fp64 angle, rounded
-    // once) into the latent rows and K's RoPE part.
+    // Group 0 copies the latent rows: their loads go out first and their stores follow the
+    // rotation, so the two memory round trips overlap.
+    constexpr int kCopies = kAppendTile * (DC / 8) / 256;
+    static_assert(kAppendTile * (DC / 8) % 256 == 0, "whole 16-byte copies per thread");
+    uint4 cp[kCopies];
     if (g == 0) {
-      for (int idx = threadIdx.x; idx < kAppendTile * (DC / 8); idx += blockDim.x) {
-        const int j = idx / (DC / 8), c8 = idx % (DC / 8);
-        const int64_t dst = s_dst[j];
-        if (dst < 0) continue;
-        *reinterpret_cast<uint4*>(latent + dst * dq + 8 * c8) =
-            *reinterpret_cast<const uint4*>(c_new + static_cast<int64_t>(n0 + j) * DC + 8 * c8);
+#pragma unroll
+      for (int u = 0; u < kCopies; ++u) {
+        const int idx = threadIdx.x + 256 * u, j = idx / (DC / 8), c8 = idx % (DC / 8);
+        const int n = min(n0 + j, a.n_tok - 1);   // past the last token: re-read it, store nothing
+        cp[u] = *reinterpret_cast<const uint4*>(c_new + static_cast<int64_t>(n) * DC + 8 * c8);
       }
     }
+    // The rotated keys of the tile (fp64 angle, rounded once), one rotation pair
+    // (kk, kk + d_R/2) per thread and step, both of its sines from one sincos.
     __shared__ bf16_t s_rope[kAppendTile * 128];
     const int half = a.dr / 2;
-    for (int idx = threadIdx.x; idx < kAppendTile * a.dr; idx += blockDim.x) {
-      const int j = idx / a.dr, k = idx % a.dr, kk = k % half;
+    for (int idx = threadIdx.x; idx < kAppendTile * half; idx += blockDim.x) {
+      const int j = idx / half, kk = idx % half;
       const int n = min(n0 + j, a.n_tok - 1);
       const int b = n / a.s_q, i = n % a.s_q;
       const double ang = static_cast<double>(a.ctx_lens[b] - a.s_q + i) * a.inv_freq[kk];
-      const double cs = cos(ang), sn = sin(ang);
+      double sn, cs;
+      sincos(ang, &sn, &cs);
       const double x1 = bf16_to_f32(kr_new[static_cast<int64_t>(n) * a.dr + kk]);
       const double x2 = bf16_to_f32(kr_new[static_cast<int64_t>(n) * a.dr + kk + half]);
-      s_rope[idx] = f32_to_bf16(static_cast<float>(k < half ? x1 * cs - x2 * sn : x1 * sn + x2 * cs));
+      s_rope[j * a.dr + kk] = f32_to_bf16(static_cast<float>(x1 * cs - x2 * sn));
+      s_rope[j * a.dr + kk + half] = f32_to_bf16(static_cast<float>(x1 * sn + x2 * cs));
+    }
+    if (g == 0) {
+#pragma unroll
+      for (int u = 0; u < kCopies; ++u) {
+        const int idx = threadIdx.x + 256 * u, j = idx / (DC / 8), c8 = idx % (DC / 8);
+        const int64_t dst = s_dst[j];
+        if (dst >= 0) *reinterpret_cast<uint4*>(latent + dst * dq + 8 * c8) = cp[u];
+      }
     }
     __syncthreads();
     for (int idx = threadIdx.x; idx < kAppendTile * a.dr; idx += blockDim.x) {
