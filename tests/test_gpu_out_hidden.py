@@ -24,6 +24,11 @@ SHAPES = {
     "llama3-8b": (32, 8, 512, 128, "bf16"),
     "dsv3": (128, 16, 512, 128, "bf16"),
     "dsv3-tp8share": (16, 2, 512, 128, "bf16"),
+    # head counts whose contraction H * d_v is 1, 10 and 19 chunks of 128: the LDS-staged
+    # form's 4-chunk ring then ends in a tail of 1, 2 and 3 chunks
+    "h1": (1, 1, 512, 128, "bf16"),
+    "h10": (10, 2, 512, 128, "bf16"),
+    "h19": (19, 1, 512, 128, "bf16"),
 }
 
 
@@ -50,6 +55,7 @@ def _dims(H, Gr, dc, dv, dtype, B, s_q):
     # 64-row LDS-staged form (hidden a multiple of 64, >= 128 workgroups): 1, 2 and 4 row
     # tiles, a ragged last tile, and two passes over the rows
     ("dsv3", 16384, 64, 1), ("dsv3", 8192, 70, 1), ("llama3-8b", 8192, 20, 1), ("llama3-8b", 16384, 13, 1),
+    ("h1", 8192, 5, 1), ("h10", 8192, 33, 1), ("h19", 16384, 17, 1),
     ("dsv3-tp8share", 2048, 9, 2),
 ])
 def test_out_hidden_matches_oracle(name, hidden, B, s_q):
