@@ -52,6 +52,9 @@ def _append(name, dtype, s_q, ctx, seed, bad_first=False, rope_shared=False):
     ("llama3-8b-b32-ctx8k", "bf16", 2, [2, 63, 64, 65, 129, 700]),
     ("dsv3-b64-ctx8k", "bf16", 1, [1, 64, 300, 4096]),
     ("dsv3-b64-ctx8k", "bf16", 4, [5, 66, 130]),
+    # several 16-token tiles, the last one ragged (22 and 18 new tokens)
+    ("llama3-8b-b32-ctx8k", "bf16", 2, [2, 63, 64, 65, 129, 700, 3, 90, 191, 257, 1000]),
+    ("dsv3-b64-ctx8k", "bf16", 2, [2, 64, 65, 127, 128, 129, 640, 641, 1500]),
 ])
 @pytest.mark.parametrize("bad_first,rope_shared", [(False, False), (True, False), (False, True)])
 def test_append_writes_exactly_the_new_slots(name, dtype, s_q, ctx, bad_first, rope_shared):
