@@ -87,7 +87,7 @@ __global__ __launch_bounds__(256) void append_tokens_kernel(AppendParams a, cons
     s_row[j * dq + e] = v;
   }
   __syncthreads();
-  if (g == 0) {
+  if (g == 0 && latent != nullptr) {
     for (int idx = threadIdx.x; idx < kAppendTile * dq; idx += blockDim.x) {
       const int j = idx / dq, e = idx % dq;
       if (s_dst[j] >= 0) Elt<T>::store(latent, s_dst[j] * dq + e, s_row[j * dq + e]);
@@ -201,12 +201,13 @@ __global__ __launch_bounds__(256) void append_tokens_mfma(AppendParams a, const 
   __syncthreads();   // s_dst
   if (static_cast<int>(blockIdx.z) == nz) {
     if (a.rope_shared && g != 0) return;   // the shared key and the latent rows are group 0's
-    // Group 0 copies the latent rows: their loads go out first and their stores follow the
-    // rotation, so the two memory round trips overlap.
+    // Group 0 copies the latent rows (when a latent cache is kept): their loads go out first
+    // and their stores follow the rotation, so the two memory round trips overlap.
     constexpr int kCopies = kAppendTile * (DC / 8) / 256;
     static_assert(kAppendTile * (DC / 8) % 256 == 0, "whole 16-byte copies per thread");
+    const bool write_latent = g == 0 && latent != nullptr;
     uint4 cp[kCopies];
-    if (g == 0) {
+    if (write_latent) {
 #pragma unroll
       for (int u = 0; u < kCopies; ++u) {
         const int idx = threadIdx.x + 256 * u, j = idx / (DC / 8), c8 = idx % (DC / 8);
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(256) void append_tokens_mfma(AppendParams a, const 
       s_rope[j * a.dr + kk] = f32_to_bf16(static_cast<float>(x1 * cs - x2 * sn));
       s_rope[j * a.dr + kk + half] = f32_to_bf16(static_cast<float>(x1 * sn + x2 * cs));
     }
-    if (g == 0) {
+    if (write_latent) {
 #pragma unroll
       for (int u = 0; u < kCopies; ++u) {
         const int idx = threadIdx.x + 256 * u, j = idx / (DC / 8), c8 = idx % (DC / 8);
@@ -253,7 +254,7 @@ __global__ __launch_bounds__(256) void append_tokens_mfma(AppendParams a, const 
         const int sl = k / kSlab, w = min(kSlab, a.dr - sl * kSlab);
         blk[static_cast<int64_t>(sl) * kBlock * kSlab + s * w + k % kSlab] = s_rope[idx];
       }
-      if (g == 0) latent[dst * dq + DC + k] = s_rope[idx];
+      if (write_latent) latent[dst * dq + DC + k] = s_rope[idx];
     }
   }
   if (!live_rows) return;

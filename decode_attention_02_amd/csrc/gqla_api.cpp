@@ -392,8 +392,10 @@ gqla_status gqla_append_tokens(const gqla_dims* dims, const gqla_paged* paged, c
   gqla_status st = check_dims(dims);
   if (st != GQLA_OK) return st;
   if ((st = check_paged(dims, paged)) != GQLA_OK) return st;
-  if (!c_new || !latent_cache || (dims->rope_dim > 0 && !kr_new))
+  if (!c_new || (dims->rope_dim > 0 && !kr_new))
     return fail(GQLA_ERR_INVALID_ARG, "null tensor pointer");
+  if (!latent_cache && !expanded_cache)
+    return fail(GQLA_ERR_INVALID_ARG, "latent_cache and expanded_cache are both NULL: nothing to write");
   if (expanded_cache && (!w_uk || !w_uv)) return fail(GQLA_ERR_INVALID_ARG, "expansion needs w_uk and w_uv");
   if (!(rope_theta > 0.f)) return fail(GQLA_ERR_INVALID_ARG, "rope_theta must be > 0");
   if (dims->rope_dim % 2 != 0) return fail(GQLA_ERR_INVALID_ARG, "rope_dim must be even (rotation pairs)");

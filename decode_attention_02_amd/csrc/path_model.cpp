@@ -3,8 +3,10 @@
 //
 // The pages' point is that the two algebraically equal forms trade cache traffic for
 // computation and that which one wins depends on the hardware ("GQLA: Attention latente
-// ...", the decode_path knob of gqla_attn.py, and the H20-3e discussion of the Chinese
-// post): the MQA-absorb path reads d_c + d_R values per token but does H * s_q dense
+// ...", English abstract; the decode_path switch of gqla_attn.py; the H20-3e comparison in
+// "GQLA: Group-Query Latent Attention for Hardware-Adaptive Decoding", Abstract, and in
+// "GQLA: Новая архитектура внимания адаптирует LLM под разное железо без переобучения"):
+// the MQA-absorb path reads d_c + d_R values per token but does H * s_q dense
 // head-products over them; the GQA path reads G * (d_qk + d_v) values per token with only
 // 16-row MFMA tiles per group. MI355X has H100-like balance (8 TB/s, 2.5 PFLOP/s bf16),
 // so the crossover sits far from the H20's.

@@ -6,13 +6,14 @@
 
 namespace gqla {
 
-// GQA split-KV decode: bf16, d_qk in {128, 192}, d_v = 128, gs * s_q <= 16.
+// GQA split-KV decode: bf16, d_qk in {128, 192}, d_v = 128, gs * s_q <= 32 (one or two
+// 16-row MFMA tiles per group); the shared-RoPE layout needs d_R = 64.
 bool tuned_gqa_supported(const gqla_dims* d);
 int tuned_gqa_target_wgs();
 int tuned_gqa_min_blocks_per_split();
 hipError_t launch_tuned_gqa(const AttnParams& p, const gqla_dims* d, hipStream_t s);
 
-// Absorb split-KV decode: bf16, d_c = 512, d_R = 64, H * s_q a multiple of 16, <= 256.
+// Absorb split-KV decode: bf16, d_c = 512, d_R = 64, H * s_q in {16, 32, 64, 128, 256, 512}.
 bool tuned_absorb_supported(const gqla_dims* d);
 int tuned_absorb_target_wgs(const gqla_dims* d);
 int tuned_absorb_min_blocks_per_split();

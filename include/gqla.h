@@ -19,7 +19,10 @@
  * --------------------------------
  * Dimensions: B batch, H query heads, G groups (G divides H; head h is in group
  * h / gs), d_c latent rank, d_R RoPE dim, d_n nope dim, d_qk = d_n + d_R, d_v value
- * dim, s_q query rows per sequence (1, or 2 for multi-token prediction).
+ * dim, s_q >= 1 query rows per sequence (1 for plain decode; 2 or more when a multi-token
+ * prediction head proposes tokens that are verified together, as the pages run the GQA path
+ * at s_q = 2). Any s_q is accepted; shapes the MFMA kernels do not cover (absorb path:
+ * H * s_q not in {16, 32, ..., 512}; GQA path: gs * s_q > 32) run on the generic kernels.
  *
  * Element type: every tensor marked "data" is float (GQLA_F32) or bfloat16 (GQLA_BF16)
  * as dims->dtype says; accumulation is always fp32. o_lat, lse and the workspace are
@@ -119,6 +122,9 @@ gqla_status gqla_absorb_query(const gqla_dims* dims, const void* q_nope, const v
  * gqla_decode_absorb — every head attends over the shared latent "key head" (step 2).
  *   s_t = scale * <q_abs[b][i][h], [c_t | kr_t]>,  o_lat = sum_t softmax(s)_t c_t,
  * over the visible tokens t of row i; split-KV with an online-softmax merge.
+ * ("GQLA: Attention latente ...", English abstract: the MQA-absorb path keeps MLA's absorbed
+ * form, in which all query heads share one latent key/value head; gqla_attn.py docstring:
+ * the absorbed path attends with a single MQA-style head per layer.)
  *   q_abs        : data [B][s_q][H][d_c + d_R]
  *   latent_cache : data [num_blocks][64][d_c + d_R]; row = [c_KV (d_c) | k_rope (d_R)]
  *   workspace    : fp32 scratch of at least gqla_workspace_bytes(.., GQLA_PATH_ABSORB)
@@ -133,6 +139,11 @@ gqla_status gqla_decode_absorb(const gqla_dims* dims, const gqla_paged* paged,
 /*
  * gqla_out_proj — apply W_UV^g to each head's latent output (step 3).
  *   out[b][i][h] = W_UV^g o_lat[b][i][h],  g = h / gs.
+ * (The value up-projection is shared by the group ("GQLA: Group-Query Latent Attention for
+ * Hardware-Adaptive Decoding", Abstract: group-shared up-projections), and applying it
+ * after the attention average instead of to every cached token gives the same result by
+ * linearity, which is what makes the absorbed form equivalent ("GQLA: Attention latente
+ * ...", English abstract; gqla_attn.py docstring, MQA-absorb path).)
  *   o_lat : fp32 [B][s_q][H][d_c];  w_uv : data [G][d_v][d_c];  out : data [B][s_q][H][d_v]
  */
 gqla_status gqla_out_proj(const gqla_dims* dims, const float* o_lat, const void* w_uv,
@@ -170,6 +181,10 @@ gqla_status gqla_expand_cache(const gqla_dims* dims, const void* latent_cache, c
  * gqla_decode_gqa — grouped-query decode over the expanded cache.
  *   out[b][i][h] = sum_t softmax(scale * <q[b][i][h], K[g]_t>)_t V[g]_t,  g = h / gs,
  * over the visible tokens t of row i; split-KV with an online-softmax merge.
+ * (The gs query heads of a group share one key head and one value head: "Grouped Query
+ * Attention (GQA)", section "Fonctionnement de la GQA"; GQLA's GQA path runs that over the
+ * latent expanded into G key/value heads: gqla_attn.py docstring, and "GQLA: Attention
+ * latente ...", English abstract, where it is the path for low-compute GPUs at s_q = 2.)
  *   q              : data [B][s_q][H][d_qk] = [q_nope | q_rope]
  *   expanded_cache : layout of gqla_expand_cache
  *   workspace      : fp32 scratch of at least gqla_workspace_bytes(.., GQLA_PATH_GQA)
@@ -194,8 +209,10 @@ gqla_status gqla_decode_gqa(const gqla_dims* dims, const gqla_paged* paged, cons
  *   kr_new         : data [B][s_q][d_R], not yet rotated (may be NULL when d_R = 0)
  *   rope_theta     : > 0 (10000 for the workloads here)
  *   w_uk, w_uv     : data [G][d_n][d_c], [G][d_v][d_c] (needed only with expanded_cache)
- *   latent_cache   : data [num_blocks][64][d_c + d_R] (updated in place)
+ *   latent_cache   : data [num_blocks][64][d_c + d_R] (updated in place), or NULL for a
+ *                    GQA-only deployment that keeps only the expanded cache
  *   expanded_cache : layout of gqla_expand_cache, or NULL for an absorb-only deployment
+ *                    (at least one of the two caches must be given)
  * Sequences with s_q > L_b or L_b beyond the table, and tokens whose block id lies outside
  * [0, num_blocks), are skipped (nothing written). Requires d_R even, d_c % 8 == 0 and
  * 64 * (d_c + d_R) <= 160 KiB; errors: GQLA_ERR_INVALID_ARG / GQLA_ERR_UNSUPPORTED.
@@ -265,7 +282,11 @@ gqla_status gqla_pick_path(const gqla_dims* dims, int64_t total_ctx, int32_t max
 
 /* Cache bytes per token per layer: latent (d_c + d_R) * elt for the absorb path,
  * G * (d_qk + d_v) * elt for the GQA path (G * (d_n + d_v) * elt + d_R * elt with
- * rope_shared); 0 for invalid arguments. */
+ * rope_shared); 0 for invalid arguments. For LLaMA-3-8B converted to GQLA the latent is
+ * 576 values against the 8-KV-head GQA baseline's 2048, 28.125% ("GQLA: Attention latente
+ * ...", English abstract); a GQA cache of 8 KV heads of 128 values is 2 * 8 * 128 * 2 B =
+ * 4 KiB per token per layer, 128 KiB over 32 layers ("Grouped Query Attention (GQA)",
+ * section "Pourquoi la GQA réduit le cache KV"). */
 int64_t gqla_cache_bytes_per_token(const gqla_dims* dims, int32_t path);
 
 /* Synchronous debug check of device-side paged metadata: copies block_table and ctx_lens

@@ -20,16 +20,19 @@ and block tables follow the workload: fixed or uniform lengths, identity or perm
 The one-eighth head share at batch 10240 fills about 190 GiB with either cache, so its two
 paths run one after the other, each with only its own cache resident.
 
-Usage: python -m decode_attention_02_amd.path_sweep [--workloads a,b] [--reps 10] [--out FILE.md]
+Usage: python path_sweep.py [--workloads a,b] [--reps 10] [--out FILE.md]
 """
 import argparse
 import json
+import os
 import sys
 
 import numpy as np
 import torch
 
-from . import _lib as L
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+
+from decode_attention_02_amd import _lib as L  # noqa: E402
 
 HBM_PEAK = 8.0e12
 MFMA_PEAK = 2.5e15

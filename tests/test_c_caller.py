@@ -23,7 +23,7 @@ int main(void) {
   gqla_paged p;
   int32_t n = -1, path = -1;
   size_t ws = 1;
-  float est = 0.f;
+  float est[2] = {0.f, 0.f};
   memset(&d, 0, sizeof d);
   memset(&p, 0, sizeof p);
   d.batch = 32; d.num_heads = 32; d.num_groups = 8; d.latent_rank = 512; d.rope_dim = 64;
@@ -38,9 +38,9 @@ int main(void) {
   CHECK(n >= 1 && n <= 128);
   CHECK(gqla_workspace_bytes(&d, &p, GQLA_PATH_ABSORB, &ws) == GQLA_OK);
   CHECK((n == 1) == (ws == 0));
-  CHECK(gqla_pick_path(&d, (int64_t)32 * 8192, 8192, &path, &est) == GQLA_OK);
+  CHECK(gqla_pick_path(&d, (int64_t)32 * 8192, 8192, &path, est) == GQLA_OK);
   CHECK(path == GQLA_PATH_ABSORB || path == GQLA_PATH_GQA);
-  CHECK(est > 0.f);
+  CHECK(est[0] > 0.f && est[1] > 0.f);   /* est_us is float[2]: {absorb, gqa} */
 
   /* Invalid dims: rejected with a message before anything is launched (no device here). */
   d.num_groups = 5;

@@ -126,3 +126,31 @@ def test_decode_after_append_matches_oracle(name, dtype, s_q, ctx, rope_shared):
         ea, eg = rel_err(got_a["out"][b], ref[b]["out"]), rel_err(got_g["out"][b], ref[b]["out"])
         log(f"  seq {b}: absorb {ea:.2e} gqa {eg:.2e}")
         assert ea <= TOL[dtype] and eg <= TOL[dtype]
+
+
+@pytest.mark.parametrize("name,dtype,s_q,ctx", [
+    ("tiny-fp32", "f32", 2, [2, 64, 65, 100]),
+    ("llama3-8b-b32-ctx8k", "bf16", 2, [2, 63, 64, 65, 129, 700, 3, 90, 191, 257, 1000]),
+    ("dsv3-tp8share-ctx16k", "bf16", 2, [2, 64, 65, 127, 1500]),
+])
+@pytest.mark.parametrize("rope_shared", [False, True])
+def test_append_without_latent_cache_writes_the_same_expanded_cache(name, dtype, s_q, ctx, rope_shared):
+    """A GQA-only deployment passes no latent cache: the expanded cache must come out bit-identical
+    to the append that also writes the latent rows."""
+    w = workload(name)
+    x = generate(w, s_q, batch=len(ctx), ctx_lens=ctx, dtype=dtype, shuffled=True, extra_blocks=2)
+    run = Run(x, 0, rope_shared)
+    expanded = run.expand()
+    exp_only = expanded.clone()
+    before = _bits(expanded)
+    rng = np.random.default_rng(21)
+    c_new = to_dev(_store(rng.standard_normal((len(ctx), s_q, w.latent)), dtype), dtype)
+    kr_new = to_dev(_store(rng.standard_normal((len(ctx), s_q, w.rope)), dtype), dtype)
+    log(f"append without latent {name} {dtype} s_q={s_q} rope_shared={rope_shared}")
+    run.G.gqla_append_tokens(run.dims, run.paged, c_new, kr_new, THETA, run.w_uk, run.w_uv, run.cache, expanded)
+    run.G.gqla_append_tokens(run.dims, run.paged, c_new, kr_new, THETA, run.w_uk, run.w_uv, None, exp_only)
+    torch.cuda.synchronize()
+    assert not np.array_equal(_bits(expanded), before)   # the append wrote something
+    assert np.array_equal(_bits(expanded), _bits(exp_only))
+    with pytest.raises(run.G.GqlaError):
+        run.G.gqla_append_tokens(run.dims, run.paged, c_new, kr_new, THETA, run.w_uk, run.w_uv, None, None)

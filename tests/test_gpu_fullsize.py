@@ -49,7 +49,14 @@ def test_fullsize_sampled(name, s_q, rope_shared):
     assert np.isfinite(got_a["out"]).all() and np.isfinite(got_g["out"]).all()
     assert np.isfinite(got_a["lse"]).all() and np.isfinite(got_g["lse"]).all()
     assert rel_err(got_a["out"], got_g["out"]) <= TOL["bf16"]
-    seqs = sorted({0, B - 1} if B > 8 else {0, B - 1})
+    # every sequence of a batch of at most 8 (the long-context batch: all its lengths and
+    # split boundaries); else the first, the last, and the shortest, a median and the
+    # longest context of the batch
+    if B <= 8:
+        seqs = list(range(B))
+    else:
+        order = np.argsort(x.ctx_lens, kind="stable")
+        seqs = sorted({0, B - 1, int(order[0]), int(order[B // 2]), int(order[-1])})
     _compare(x, got_a, got_g, seqs, name)
 
 

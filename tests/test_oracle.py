@@ -106,6 +106,47 @@ def test_gqa_path_matches_sdpa(name, s_q, ctx):
                 assert abs(ref - lse[i, h]) < 1e-12
 
 
+def _scale_pin_passes(M, name):
+    """M's definition and absorb path, each at M.qk_scale(d_n, d_R), against torch SDPA left
+    at its DEFAULT scale (no scale= argument: SDPA divides by the square root of the query
+    width E, here the non-absorbed head width d_n + d_R of the [q_nope | q_rope] queries).
+    The module's constructor fixes the same value (GQLAAttention scales by
+    head_dim ** -0.5). The workloads' latent widths d_c + d_R (80, 576) differ from
+    d_n + d_R (48, 192), so an absorbed-width scale cannot pass."""
+    w = workload(name)
+    s_q = 2
+    x = generate(w, s_q, batch=1, ctx_lens=[37])
+    c, kr, wk, wv, qn, qr, q = _f64_inputs(x)
+    sc = M.qk_scale(w.nope, w.rope)
+    K, V = R.expand_latent(c[0], kr[0], wk, wv)
+    L = K.shape[1]
+    mask = torch.arange(L)[None, :] <= (L - s_q + torch.arange(s_q))[:, None]
+    rep = w.heads // w.groups
+    qt = torch.from_numpy(np.ascontiguousarray(q[0].transpose(1, 0, 2)))[None]
+    kt = torch.from_numpy(np.ascontiguousarray(K))[None].repeat_interleave(rep, dim=1)
+    vt = torch.from_numpy(np.ascontiguousarray(V))[None].repeat_interleave(rep, dim=1)
+    assert qt.shape[-1] == w.nope + w.rope
+    ref = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask)[0].numpy().transpose(1, 0, 2)
+    out, _ = M.mla_expanded_attention(c[0], kr[0], wk, wv, qn[0], qr[0], s_q, sc)
+    ab = M.batch_absorb(c, kr, wk, wv, qn, qr, s_q, sc)[0][3]
+    return _rel(out, ref) < 1e-12 and _rel(ab, ref) < 1e-12
+
+
+@pytest.mark.parametrize("name", ["tiny-fp32", "dsv3-b64-ctx8k"])
+def test_qk_scale_is_sdpa_default_scale(name):
+    """Softmax scale pin: qk_scale(d_n, d_R) is the scale torch SDPA applies by default to
+    the non-absorbed queries, 1/sqrt(d_n + d_R) (the module's head_dim ** -0.5)."""
+    assert _scale_pin_passes(R, name)
+
+
+@pytest.mark.parametrize("name", ["tiny-fp32", "dsv3-b64-ctx8k"])
+def test_scale_pin_catches_absorbed_width_scale(name):
+    """Planted mistake: scaling by the absorbed key width, 1/sqrt(d_c + d_R), fails."""
+    w = workload(name)
+    M = _mutant(qk_scale=lambda d_n, d_r: 1.0 / math.sqrt(w.latent + d_r))
+    assert not _scale_pin_passes(M, name)
+
+
 @pytest.mark.parametrize("s_q", [1, 2])
 def test_one_token_context_returns_value_exactly(s_q):
     """With one visible token the softmax weight is exactly 1: out = V_0 and o_lat = c_0
