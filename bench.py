@@ -119,9 +119,9 @@ def summarize_pmc(fetch_dir, write_dir, workload_name, layout):
             "dispatches": len(f[gqa[0]]),
             "calibration": {"copy_kernel": big, "bytes": CALIB_BYTES, "fetch_scale": f_scale, "write_scale": w_scale},
             "commands": [f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <FETCH_DIR> -o run -- python3 bench.py "
-                         f"--profile --workload {workload_name} --gqa-layout {layout} --paths gqa",
+                         f"--profile --workload {workload_name} --gqa-layout {layout} --paths gqa --no-cpu-baseline",
                          f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <WRITE_DIR> -o run -- python3 bench.py "
-                         f"--profile --workload {workload_name} --gqa-layout {layout} --paths gqa",
+                         f"--profile --workload {workload_name} --gqa-layout {layout} --paths gqa --no-cpu-baseline",
                          f"python bench.py --summarize-pmc <FETCH_DIR> <WRITE_DIR> --workload {workload_name} "
                          f"--gqa-layout {layout} --store-traffic"]}
 
@@ -455,7 +455,7 @@ def cpu_baseline(bn, budget_s):
             "sample": f"GQA path (expansion of the sequence's latent + grouped attention, s_q={bn.s_q}) on {n_g} "
                       f"decodes of {len(bn.sample)} seeded sample sequences of the batch (context "
                       f"{int(bn.lens_h[bn.sample].min())}-{int(bn.lens_h[bn.sample].max())}), fp64 NumPy, "
-                      f"{t_g:.1f} s; extrapolated to the whole batch of {bn.B}: {full_s:.0f} s per step",
+                      f"{t_g:.1f} s (the absorb path timed alongside); extrapolated to the whole batch of {bn.B}: {full_s:.0f} s per step",
             "extrapolated_full_batch_s": full_s,
             "absorb_path": {"tokens_per_s": n_a * bn.abs_s_q / t_a, "decodes": n_a, "seconds": t_a,
                             "s_q": bn.abs_s_q},
@@ -529,7 +529,7 @@ def main(argv=None):
             res_paths["gqa"] = path_record(bn, "gqa", r, bn.kv_gqa, vis(bn.s_q) * w.heads * 2 * (w.qk + w.v),
                                            bn.s_q, n_split)
             log(f"[bench] GQA step {r['ms']:.3f} ms (median {r['median_ms']:.3f}, best {r['best_ms']:.3f}); "
-                f"decode {r['decode_ms']:.3f} ms = {bn.kv_gqa / r['decode_ms'] / 1e9:.0f} GB/s")
+                f"decode {r['decode_ms']:.3f} ms = {bn.kv_gqa / r['decode_ms'] / 1e6:.0f} GB/s")
         bn.free_gqa()
     if "absorb" in paths:
         bn.setup_absorb()
@@ -546,7 +546,7 @@ def main(argv=None):
                                               vis(bn.abs_s_q) * w.heads * 2 * (2 * w.latent + w.rope),
                                               bn.abs_s_q, n_split)
             log(f"[bench] absorb step {r['ms']:.3f} ms (median {r['median_ms']:.3f}, best {r['best_ms']:.3f}); "
-                f"decode {r['decode_ms']:.3f} ms = {bn.kv_abs / r['decode_ms'] / 1e9:.0f} GB/s")
+                f"decode {r['decode_ms']:.3f} ms = {bn.kv_abs / r['decode_ms'] / 1e6:.0f} GB/s")
         bn.free_absorb()
     if a.profile:
         log("[bench] profile passes done")
