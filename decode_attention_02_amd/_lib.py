@@ -22,7 +22,8 @@ EXPORTED = ("gqla_absorb_query", "gqla_decode_absorb", "gqla_out_proj", "gqla_ex
             "gqla_decode_gqa", "gqla_num_splits", "gqla_workspace_bytes",
             "gqla_cache_bytes_per_token", "gqla_validate_paged", "gqla_status_string",
             "gqla_last_error", "gqla_version", "gqla_pick_path", "gqla_append_tokens",
-            "gqla_out_hidden", "gqla_fold_out_weight")
+            "gqla_out_hidden", "gqla_fold_out_weight", "gqla_decode_absorb_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20   # GQLA_NOALLOC_SCRATCH_BYTES
 
 
 class GqlaError(RuntimeError):
@@ -56,6 +57,7 @@ def _load() -> ctypes.CDLL:
     sig = {
         "gqla_absorb_query": [D, vp, vp, vp, vp, vp],
         "gqla_decode_absorb": [D, P, vp, vp, vp, sz, vp, vp, vp],
+        "gqla_decode_absorb_noalloc": [D, P, vp, vp, vp, vp, vp],
         "gqla_out_proj": [D, vp, vp, vp, vp],
         "gqla_expand_cache": [D, vp, vp, vp, vp, i64, i64, vp, vp],
         "gqla_decode_gqa": [D, P, vp, vp, vp, sz, vp, vp, vp],
@@ -154,6 +156,15 @@ def gqla_decode_absorb(dims: Dims, paged: Paged, q_abs, latent_cache, workspace,
     _check(LIB.gqla_decode_absorb(ctypes.byref(d), ctypes.byref(p), _ptr(q_abs), _ptr(latent_cache),
                                   _ptr(workspace), ws_bytes, _ptr(o_lat), _ptr(lse), _stream(stream)),
            "gqla_decode_absorb")
+
+
+def gqla_decode_absorb_noalloc(dims: Dims, paged: Paged, q_abs, latent_cache, o_lat, lse=None,
+                               stream=None) -> None:
+    """gqla_decode_absorb with the split partials in the library's fixed scratch array."""
+    d, p = dims.c(), paged.c()
+    _check(LIB.gqla_decode_absorb_noalloc(ctypes.byref(d), ctypes.byref(p), _ptr(q_abs), _ptr(latent_cache),
+                                          _ptr(o_lat), _ptr(lse), _stream(stream)),
+           "gqla_decode_absorb_noalloc")
 
 
 def gqla_out_proj(dims: Dims, o_lat, w_uv, out, stream=None) -> None:

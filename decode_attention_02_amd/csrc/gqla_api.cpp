@@ -27,6 +27,12 @@ gqla_status fail(gqla_status s, const char* fmt, ...) {
   return s;
 }
 
+}  // namespace
+
+void gqla::set_last_error(const char* msg) { g_err = msg; }
+
+namespace {
+
 gqla_status hip_fail(hipError_t e, const char* where) {
   return fail(GQLA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
 }

@@ -8,6 +8,9 @@ struct gqla_dims;   // include/gqla.h
 
 namespace gqla {
 
+// Message returned by gqla_last_error() on the calling thread (gqla_api.cpp).
+void set_last_error(const char* msg);
+
 constexpr int kBlock = 64;        // tokens per cache block
 constexpr int kSlab = 32;         // key features per slab of the expanded cache
 constexpr int kHalf = 32;         // tokens per value half-slab of the expanded cache

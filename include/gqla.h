@@ -137,6 +137,27 @@ gqla_status gqla_decode_absorb(const gqla_dims* dims, const gqla_paged* paged,
                                size_t workspace_bytes, float* o_lat, float* lse, void* stream);
 
 /*
+ * gqla_decode_absorb_noalloc — gqla_decode_absorb without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). The split-KV partial results go to a fixed scratch array
+ * of GQLA_NOALLOC_SCRATCH_BYTES in the library's own device memory, one per GPU, held from
+ * the library's load until the process ends; the call itself allocates nothing.
+ *   Arguments and results are those of gqla_decode_absorb (same kernels, same outputs).
+ *   The scratch of the calling thread's current device is used: `stream` must belong to it.
+ *   Its address is looked up on the first call on each device; make that first call outside
+ *   graph capture.
+ *   Calls that overlap on one GPU (on different streams, or from several threads) share the
+ *   array and race: serialise them. Nothing in it needs clearing between calls.
+ * Errors: those of gqla_decode_absorb, and GQLA_ERR_WORKSPACE when the split plan needs more
+ * than GQLA_NOALLOC_SCRATCH_BYTES (B * s_q * H * n_split * (d_c + 1) * 4 bytes; e.g. LLaMA-3-8B
+ * batch 32 at s_q = 1 needs 16.8 MB, the DeepSeek-V3 long-context batch of 8 at s_q = 2 needs
+ * 33.6 MB; see gqla_workspace_bytes).
+ */
+#define GQLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+gqla_status gqla_decode_absorb_noalloc(const gqla_dims* dims, const gqla_paged* paged, const void* q_abs,
+                                       const void* latent_cache, float* o_lat, float* lse, void* stream);
+
+/*
  * gqla_out_proj — apply W_UV^g to each head's latent output (step 3).
  *   out[b][i][h] = W_UV^g o_lat[b][i][h],  g = h / gs.
  * (The value up-projection is shared by the group ("GQLA: Group-Query Latent Attention for
