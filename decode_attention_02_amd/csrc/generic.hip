@@ -165,9 +165,11 @@ hipError_t launch_generic_attn(const AttnParams& p, bool bf16, hipStream_t s) {
 // consecutive features with 16-byte loads, eight splits at a time: the loads of a batch
 // are issued together and an empty split (lse = -inf) is skipped by its weight, not by a
 // branch around its load.
+constexpr int kMaxCombineSplits = 1024;   // the split plans never exceed this many per row
+
 __global__ __launch_bounds__(128) void combine_splits(CombineParams c) {
   const int64_t row = blockIdx.x;
-  const float* lse = c.ws_lse + row * c.n_split;
+  const float* lse = c.ws_lse + row * c.n_split;   // re-pointed at LDS on the general path
   constexpr int kFew = 8;
   if ((c.dvo & 3) == 0 && c.n_split <= kFew) {
     // Up to 8 splits: the split lse values and the partial outputs load together (one
@@ -206,6 +208,12 @@ __global__ __launch_bounds__(128) void combine_splits(CombineParams c) {
     }
     return;
   }
+  // More splits: the row's lse values are staged in LDS by one parallel load, so the loops
+  // over them below do not wait for a memory round trip per split.
+  __shared__ float s_lse[kMaxCombineSplits];
+  for (int s = threadIdx.x; s < c.n_split; s += blockDim.x) s_lse[s] = lse[s];
+  __syncthreads();
+  lse = s_lse;
   float m = -INFINITY;
   bool has_nan = false;
   for (int s = 0; s < c.n_split; ++s) {
@@ -226,10 +234,12 @@ __global__ __launch_bounds__(128) void combine_splits(CombineParams c) {
     for (int f = 4 * threadIdx.x; f < c.dvo; f += 4 * blockDim.x) {
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
       for (int s0 = 0; s0 < c.n_split; s0 += kBatch) {
+        // Empty slots (lse = -inf: a split past the sequence's end) are not loaded.
         float4 v[kBatch];
 #pragma unroll
         for (int j = 0; j < kBatch; ++j)
-          if (s0 + j < c.n_split) v[j] = *reinterpret_cast<const float4*>(o + static_cast<int64_t>(s0 + j) * c.dvo + f);
+          if (s0 + j < c.n_split && lse[s0 + j] != -INFINITY)
+            v[j] = *reinterpret_cast<const float4*>(o + static_cast<int64_t>(s0 + j) * c.dvo + f);
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
           if (s0 + j < c.n_split) {
@@ -259,6 +269,7 @@ __global__ __launch_bounds__(128) void combine_splits(CombineParams c) {
 }
 
 hipError_t launch_combine(const CombineParams& c, hipStream_t s) {
+  if (c.n_split > kMaxCombineSplits) return hipErrorInvalidValue;
   combine_splits<<<c.rows, 128, 0, s>>>(c);
   return hipGetLastError();
 }

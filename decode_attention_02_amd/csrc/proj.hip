@@ -55,16 +55,32 @@ __device__ __forceinline__ int swz(int r) { return 2 * ((r & 3) | (((r >> 3) & 1
 
 // NW waves per workgroup, 16 rows each: 4 when the rows are many (the staged weight slice
 // serves 64 rows), 1 when 64-row workgroups would leave most CUs idle.
+// Workgroup ids are laid out so that the NZ workgroups sharing one row tile (the feature
+// slices of the absorbed query, the output quarters of the value projection) have ids 8
+// apart: the dispatcher places them on the same XCD at about the same time, and the rows
+// they all read come from that XCD's L2 after the first. Returns (x, g, z) for a grid of
+// nx * G * NZ workgroups (nx a multiple of 8).
+struct GridPos {
+  int x, g, z;
+};
+__device__ __forceinline__ GridPos grid_pos(int G, int NZ) {
+  const int id = blockIdx.x, xcd = id & 7, rest = id >> 3;
+  const int z = rest % NZ, r2 = rest / NZ;
+  return {(r2 / G) * 8 + xcd, r2 % G, z};
+}
+
 template <int DN, int NW>
 __global__ __launch_bounds__(NW * 64) void absorb_query_kernel(ProjParams d, const bf16_t* q_nope, const bf16_t* q_rope,
-                                                               const bf16_t* w_uk, bf16_t* q_abs) {
+                                                               const bf16_t* w_uk, bf16_t* q_abs, int nx) {
   __shared__ __attribute__((aligned(16))) char w[DN * kSliceF * 2];
   constexpr int RW = 16 * NW;   // rows per workgroup pass
-  const int g = blockIdx.z;
-  const int f0 = blockIdx.x * kSliceF;
+  const GridPos gp = grid_pos(d.G, kDC / kSliceF);
+  const int g = gp.g;
+  const int f0 = gp.z * kSliceF;
   const int gs = d.H / d.G;
   const int rows_g = d.rows * gs;
   const int n_rt = (rows_g + RW - 1) / RW;
+  if (gp.x >= n_rt) return;   // a lane of the rounded-up grid with no row tile: no copy issued
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
   constexpr int KS = DN / 32;
@@ -86,7 +102,7 @@ __global__ __launch_bounds__(NW * 64) void absorb_query_kernel(ProjParams d, con
   const int src_n = 8 * grp + (col >> 2);
   const int src_b = 8 * (col & 3);   // byte offset inside the 32-byte feature tile
   bool staged = false;
-  for (int rt = blockIdx.y; rt < n_rt; rt += gridDim.y) {
+  for (int rt = gp.x; rt < n_rt; rt += nx) {
     const int rg = rt * RW + wave * 16 + col;   // this lane's row (B operand column)
     const bool live = rg < rows_g;
     const int64_t row = group_row(live ? rg : rows_g - 1, g, gs, d.H);   // past the end: re-read the last row
@@ -121,7 +137,7 @@ __global__ __launch_bounds__(NW * 64) void absorb_query_kernel(ProjParams d, con
     }
     // The RoPE part is a copy (64 values = 8 chunks of 16 bytes per row), done by the
     // first feature slice.
-    if (blockIdx.x == 0) {
+    if (gp.z == 0) {
       for (int i = threadIdx.x; i < RW * (kDR / 8); i += blockDim.x) {
         const int r = rt * RW + i / (kDR / 8), c = i % (kDR / 8);
         if (r >= rows_g) continue;
@@ -133,12 +149,15 @@ __global__ __launch_bounds__(NW * 64) void absorb_query_kernel(ProjParams d, con
   }
 }
 
-__global__ __launch_bounds__(64) void out_proj_kernel(ProjParams d, const float* o_lat, const bf16_t* w_uv, bf16_t* out) {
-  const int g = blockIdx.y;
+__global__ __launch_bounds__(64) void out_proj_kernel(ProjParams d, const float* o_lat, const bf16_t* w_uv, bf16_t* out,
+                                                      int nx) {
+  const GridPos gp = grid_pos(d.G, kDV / 32);
+  const int g = gp.g;
   const int gs = d.H / d.G;
   const int rows_g = d.rows * gs;
   const int n_rt = (rows_g + 15) / 16;
-  const int lane = threadIdx.x, wave = blockIdx.z;   // one wave per workgroup: its 32 rows of W_UV^g
+  if (gp.x >= n_rt) return;   // a lane of the rounded-up grid with no row tile
+  const int lane = threadIdx.x, wave = gp.z;   // one wave per workgroup: its 32 rows of W_UV^g
   const int col = lane & 15, grp = lane >> 4;
   // A operand, kept for every row tile: W_UV^g rows 32*wave + 16*t + col, latent values
   // 32*ks + 8*grp .. +8.
@@ -151,7 +170,7 @@ __global__ __launch_bounds__(64) void out_proj_kernel(ProjParams d, const float*
       for (int ks = 0; ks < kDC / 32; ++ks)
         wa[t][ks] = *reinterpret_cast<const bf16x8*>(wsrc + 16 * t * kDC + 32 * ks);
   }
-  for (int rt = blockIdx.x; rt < n_rt; rt += gridDim.x) {
+  for (int rt = gp.x; rt < n_rt; rt += nx) {
     const int rg = rt * 16 + col;
     const bool live = rg < rows_g;
     // Lanes past the last row read the last row (loads stay unconditional, so the whole
@@ -210,17 +229,20 @@ hipError_t launch_tuned_absorb_query(const ProjParams& p, const void* q_nope, co
   const int per_row = (kDC / kSliceF) * p.G;
   const bool wide = static_cast<int64_t>((rows_g + 63) / 64) * per_row >= kNumCUs;
   const int n_rt = wide ? (rows_g + 63) / 64 : (rows_g + 15) / 16;
-  dim3 grid(kDC / kSliceF, std::max(1, std::min(n_rt, kMaxWGs / per_row)), p.G);
+  const int nx = (std::max(1, std::min(n_rt, kMaxWGs / per_row)) + 7) / 8 * 8;   // row-tile lanes, x8 for grid_pos
+  const int64_t wgs = static_cast<int64_t>(nx) * per_row;
+  if (wgs > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<unsigned>(wgs));
   const bf16_t* qn = static_cast<const bf16_t*>(q_nope);
   const bf16_t* qr = static_cast<const bf16_t*>(q_rope);
   const bf16_t* wk = static_cast<const bf16_t*>(w_uk);
   bf16_t* qa = static_cast<bf16_t*>(q_abs);
   if (wide) {
-    if (p.dn == 128) absorb_query_kernel<128, 4><<<grid, 256, 0, s>>>(p, qn, qr, wk, qa);
-    else absorb_query_kernel<64, 4><<<grid, 256, 0, s>>>(p, qn, qr, wk, qa);
+    if (p.dn == 128) absorb_query_kernel<128, 4><<<grid, 256, 0, s>>>(p, qn, qr, wk, qa, nx);
+    else absorb_query_kernel<64, 4><<<grid, 256, 0, s>>>(p, qn, qr, wk, qa, nx);
   } else {
-    if (p.dn == 128) absorb_query_kernel<128, 1><<<grid, 64, 0, s>>>(p, qn, qr, wk, qa);
-    else absorb_query_kernel<64, 1><<<grid, 64, 0, s>>>(p, qn, qr, wk, qa);
+    if (p.dn == 128) absorb_query_kernel<128, 1><<<grid, 64, 0, s>>>(p, qn, qr, wk, qa, nx);
+    else absorb_query_kernel<64, 1><<<grid, 64, 0, s>>>(p, qn, qr, wk, qa, nx);
   }
   return hipGetLastError();
 }
@@ -237,8 +259,11 @@ hipError_t launch_tuned_out_proj(const ProjParams& p, const float* o_lat, const 
   // with many row tiles a wave visits at least 4 of them so that weight reloads stay small
   // next to the latent-output reads.
   const int want = std::max((n_rt + 3) / 4, 256 / p.G);
-  dim3 grid(std::max(1, std::min({n_rt, want, kMaxWGs / p.G})), p.G, kDV / 32);
-  out_proj_kernel<<<grid, 64, 0, s>>>(p, o_lat, static_cast<const bf16_t*>(w_uv), static_cast<bf16_t*>(out));
+  const int nx = (std::max(1, std::min({n_rt, want, kMaxWGs / p.G})) + 7) / 8 * 8;   // x8 for grid_pos
+  const int64_t wgs = static_cast<int64_t>(nx) * p.G * (kDV / 32);
+  if (wgs > 0x7fffffff) return hipErrorInvalidConfiguration;
+  out_proj_kernel<<<static_cast<unsigned>(wgs), 64, 0, s>>>(p, o_lat, static_cast<const bf16_t*>(w_uv),
+                                                            static_cast<bf16_t*>(out), nx);
   return hipGetLastError();
 }
 
