@@ -63,12 +63,12 @@ __device__ __forceinline__ float xor_sum(float v) {
 // workgroups of one sequence's groups are placed on one XCD so that area is fetched from
 // HBM once and served to the other groups from that XCD's L2.
 template <int DQK, int DV, int kWaves, int RT, bool SHARED>
-__global__ __launch_bounds__(kWaves * 64) void gqa_decode_split(AttnParams p) {
+__global__ __launch_bounds__(kWaves * 64, RT == 1 ? 2 : 1) void gqa_decode_split(AttnParams p) {
   constexpr int KS = DQK / 32;     // k-steps of the score product
   constexpr int KSN = SHARED ? (DQK - 64) / 32 : KS;   // k-steps held in the group chunk
   constexpr int KF = 32 * KSN;     // K features in the group chunk
   constexpr int NT = DV / 16;      // feature tiles of the value product
-  constexpr bool kHalfUnits = (RT == 2 && DQK > 128) || kWaves == 8;
+  constexpr bool kHalfUnits = (RT == 2 && DQK > 128) || RT == 1;
   __shared__ float s_o[kWaves][RT][NT][64][4];   // per-wave O^T fragments (lane-major)
   __shared__ float s_m[kWaves][RT * 16];
   __shared__ float s_l[kWaves][RT * 16];
@@ -267,8 +267,8 @@ __global__ __launch_bounds__(kWaves * 64) void gqa_decode_split(AttnParams p) {
     }
   } else {
     // Two half blocks in flight (the next half's loads issued before the current half is
-    // consumed): the register budget of two row tiles at d_qk = 192, and of two waves per
-    // SIMD in the 8-wave workgroups.
+    // consumed): the register budget of two row tiles at d_qk = 192, and of two workgroups
+    // per CU (two waves per SIMD) with one row tile.
     if (n_my > 0) {
       const int nu = 2 * n_my;
       auto unit_chunk = [&](int u) { return chunk_of(block_id(min(u, nu - 1) >> 1)); };
@@ -368,13 +368,16 @@ bool tuned_gqa_supported(const gqla_dims* d) {
 int tuned_gqa_target_wgs() { return kNumCUs; }
 int tuned_gqa_min_blocks_per_split() { return 8; }
 
-// One row tile: 8 waves (two per SIMD, half a block in flight each), which keeps the same
-// bytes in flight as 4 waves with two blocks each but lets one wave's loads run while the
-// other does its softmax (4.5% faster on the long-context batch, equal on LLaMA-3-8B).
-// Two row tiles need the registers of one wave per SIMD.
+// Four waves per workgroup. With one row tile each wave keeps half a block in flight within
+// 256 registers, so two workgroups share a CU (two waves per SIMD): one wave's loads run while
+// the other does its softmax, and one workgroup streams while the other starts (block ids,
+// queries, first block) or merges its waves. Against one 8-wave workgroup per CU with the same
+// per-wave code: LLaMA-3-8B batch 32 131.5 -> 126.8 us, DeepSeek-V3 batch 64 675 -> 655 us,
+// the long-context batch equal, the 1/8 DeepSeek-V3 share 29.14 -> 28.99 ms. Two row tiles
+// need the registers of one wave per SIMD.
 template <int DQK, int RT, bool SHARED>
 hipError_t launch_dqk(const AttnParams& p, hipStream_t s) {
-  constexpr int kWaves = RT == 1 ? 8 : 4;
+  constexpr int kWaves = 4;
   const int64_t units = static_cast<int64_t>(p.B) * p.n_split;
   const int64_t wgs = SHARED ? (units + 7) / 8 * 8 * p.kv_heads : units * p.kv_heads;
   if (wgs > 0x7fffffff) return hipErrorInvalidConfiguration;

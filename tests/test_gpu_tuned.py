@@ -150,3 +150,20 @@ def test_absorb_one_token_context_is_latent_row():
         c0 = x.f64(x.c_kv_seq[b][0])
         for h in range(w.heads):
             assert np.array_equal(got["o_lat"][b, 0, h], c0), (b, h)
+
+
+@pytest.mark.parametrize("heads,groups,s_q", [(24, 3, 2), (8, 1, 2), (8, 1, 1), (48, 6, 1)])
+@pytest.mark.parametrize("rope_shared", [False, True])
+def test_gqa_decode_group_counts_match_oracle(heads, groups, s_q, rope_shared):
+    """Even group counts are served two groups per workgroup with the shared RoPE key, odd
+    ones (3, and MQA's single group) one per workgroup: both forms against the oracle."""
+    w = workload("dsv3-b64-ctx8k", heads=heads, groups=groups)
+    x = generate(w, s_q, batch=5, ctx_lens=[s_q, 64, 65, 700, 1500], shuffled=True, extra_blocks=2)
+    log(f"gqa groups={groups} heads={heads} s_q={s_q} rope_shared={rope_shared}")
+    got = Run(x, 0, rope_shared).gqa()
+    ref = oracle_paths(x)
+    for b in ref:
+        e = rel_err(got["out"][b], ref[b]["out"])
+        le = float(np.max(np.abs(got["lse"][b] - ref[b]["lse"])))
+        log(f"  seq {b} L={int(x.ctx_lens[b])}: out {e:.2e} lse_abs {le:.2e}")
+        assert e <= TOL["bf16"] and le <= TOL["bf16"] * max(1.0, float(np.max(np.abs(ref[b]["lse"]))))
