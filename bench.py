@@ -316,9 +316,9 @@ class Bench:
                              self.latent, None)
         G.gqla_absorb_query(self.d_abs, self.q_nope, self.q_rope, self.w_uk, self.q_abs)
         if ev: ev[1].record()
-        G.gqla_decode_absorb(self.d_abs, self.paged, self.q_abs, self.latent, self.ws_a, self.o_lat)
+        G.gqla_decode_absorb_out(self.d_abs, self.paged, self.q_abs, self.latent, self.w_uv, self.ws_a, self.o_lat,
+                                 self.out_a)
         if ev: ev[2].record()
-        G.gqla_out_proj(self.d_abs, self.o_lat, self.w_uv, self.out_a)
 
     def free_absorb(self):
         del self.latent, self.q_abs, self.o_lat, self.out_a, self.ws_a
@@ -474,9 +474,10 @@ def path_record(bn, name, r, kv, flops, s_q, splits):
         d["step"] = "gqla_append_tokens (expanded cache only) + gqla_decode_gqa"
         d["append_ms"] = r["pre_decode_ms"]
     else:
-        d["step"] = "gqla_append_tokens (latent cache) + gqla_absorb_query + gqla_decode_absorb + gqla_out_proj"
+        d["step"] = ("gqla_append_tokens (latent cache) + gqla_absorb_query + gqla_decode_absorb_out (decode, then "
+                     "the split combine fused with W_UV^g)")
         d["append_and_query_ms"] = r["pre_decode_ms"]
-        d["out_proj_ms"] = r["post_decode_ms"]
+        d["decode_includes"] = "the split combine and the W_UV^g value projection"
     return d
 
 

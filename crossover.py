@@ -2,7 +2,7 @@
 
 For each layer shape and s_q it times one decode step of each GQLA path on random data
 (the same work bench.py counts in a step):
-  absorb: gqla_absorb_query -> gqla_decode_absorb (+ combine) -> gqla_out_proj
+  absorb: gqla_absorb_query -> gqla_decode_absorb_out (decode; combine fused with W_UV^g)
   GQA:    gqla_expand_cache of the blocks holding the new tokens -> gqla_decode_gqa
 and prints one JSON line per case plus a markdown table. The shapes are the DeepSeek-V3
 attention layer and its 1/R tensor-parallel head shares (H = 128/R query heads in
@@ -82,8 +82,7 @@ def run_case(name, s_q, batch, ctx, reps, gen, rope_shared=1):
 
     def absorb():
         L.gqla_absorb_query(d, q_nope, q_rope, w_uk, q_abs)
-        L.gqla_decode_absorb(d, paged, q_abs, latent, ws_a, o_lat)
-        L.gqla_out_proj(d, o_lat, w_uv, out)
+        L.gqla_decode_absorb_out(d, paged, q_abs, latent, w_uv, ws_a, o_lat, out)
 
     t_abs = _median_us(absorb, reps)
     expanded = torch.empty(nb * 64 * L.gqla_cache_bytes_per_token(d, L.GQLA_PATH_GQA) // 2,

@@ -22,7 +22,8 @@ EXPORTED = ("gqla_absorb_query", "gqla_decode_absorb", "gqla_out_proj", "gqla_ex
             "gqla_decode_gqa", "gqla_num_splits", "gqla_workspace_bytes",
             "gqla_cache_bytes_per_token", "gqla_validate_paged", "gqla_status_string",
             "gqla_last_error", "gqla_version", "gqla_pick_path", "gqla_append_tokens",
-            "gqla_out_hidden", "gqla_fold_out_weight", "gqla_decode_absorb_noalloc")
+            "gqla_out_hidden", "gqla_fold_out_weight", "gqla_decode_absorb_noalloc",
+            "gqla_decode_absorb_out")
 NOALLOC_SCRATCH_BYTES = 64 << 20   # GQLA_NOALLOC_SCRATCH_BYTES
 
 
@@ -58,6 +59,7 @@ def _load() -> ctypes.CDLL:
         "gqla_absorb_query": [D, vp, vp, vp, vp, vp],
         "gqla_decode_absorb": [D, P, vp, vp, vp, sz, vp, vp, vp],
         "gqla_decode_absorb_noalloc": [D, P, vp, vp, vp, vp, vp],
+        "gqla_decode_absorb_out": [D, P, vp, vp, vp, vp, sz, vp, vp, vp, vp],
         "gqla_out_proj": [D, vp, vp, vp, vp],
         "gqla_expand_cache": [D, vp, vp, vp, vp, i64, i64, vp, vp],
         "gqla_decode_gqa": [D, P, vp, vp, vp, sz, vp, vp, vp],
@@ -165,6 +167,16 @@ def gqla_decode_absorb_noalloc(dims: Dims, paged: Paged, q_abs, latent_cache, o_
     _check(LIB.gqla_decode_absorb_noalloc(ctypes.byref(d), ctypes.byref(p), _ptr(q_abs), _ptr(latent_cache),
                                           _ptr(o_lat), _ptr(lse), _stream(stream)),
            "gqla_decode_absorb_noalloc")
+
+
+def gqla_decode_absorb_out(dims: Dims, paged: Paged, q_abs, latent_cache, w_uv, workspace, o_lat, out, lse=None,
+                           stream=None) -> None:
+    """gqla_decode_absorb then gqla_out_proj in one call (split combine fused with W_UV^g)."""
+    d, p = dims.c(), paged.c()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(LIB.gqla_decode_absorb_out(ctypes.byref(d), ctypes.byref(p), _ptr(q_abs), _ptr(latent_cache), _ptr(w_uv),
+                                      _ptr(workspace), ws_bytes, _ptr(o_lat), _ptr(out), _ptr(lse), _stream(stream)),
+           "gqla_decode_absorb_out")
 
 
 def gqla_out_proj(dims: Dims, o_lat, w_uv, out, stream=None) -> None:

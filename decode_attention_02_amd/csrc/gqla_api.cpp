@@ -125,9 +125,11 @@ size_t workspace_for(const gqla_dims* d, int32_t path, int n_split) {
   return rows * n_split * (dvo + 1) * sizeof(float);
 }
 
+// The split-KV decode of either path; with skip_combine the partials are left in the
+// workspace for a fused consumer (gqla_decode_absorb_out).
 gqla_status run_decode(const gqla_dims* d, const gqla_paged* pg, int32_t path, const void* q,
                        const void* cache, void* ws, size_t ws_bytes, void* out, int32_t out_kind,
-                       float* lse, void* stream) {
+                       float* lse, void* stream, bool skip_combine = false) {
   const Plan pl = plan(d, pg, path);
   const size_t need = workspace_for(d, path, pl.n_split);
   if (ws_bytes < need || (need > 0 && ws == nullptr))
@@ -202,7 +204,7 @@ gqla_status run_decode(const gqla_dims* d, const gqla_paged* pg, int32_t path, c
     e = gqla::launch_generic_attn(a, bf16, s);
   }
   if (e != hipSuccess) return hip_fail(e, gqa ? "gqa split-KV decode launch" : "absorb split-KV decode launch");
-  if (pl.n_split > 1) {
+  if (pl.n_split > 1 && !skip_combine) {
     gqla::CombineParams c{a.ws_o, a.ws_lse, rows, pl.n_split, a.dvo, out, out_kind, lse};
     e = gqla::launch_combine(c, s);
     if (e != hipSuccess) return hip_fail(e, "split-KV combine launch");
@@ -250,6 +252,32 @@ gqla_status gqla_decode_absorb(const gqla_dims* dims, const gqla_paged* paged, c
   if (!q_abs || !latent_cache || !o_lat) return fail(GQLA_ERR_INVALID_ARG, "null tensor pointer");
   return run_decode(dims, paged, GQLA_PATH_ABSORB, q_abs, latent_cache, workspace, workspace_bytes,
                     o_lat, gqla::OUT_F32, lse, stream);
+}
+
+gqla_status gqla_decode_absorb_out(const gqla_dims* dims, const gqla_paged* paged, const void* q_abs,
+                                   const void* latent_cache, const void* w_uv, void* workspace,
+                                   size_t workspace_bytes, float* o_lat, void* out, float* lse, void* stream) {
+  gqla_status st = check_dims(dims);
+  if (st != GQLA_OK) return st;
+  if ((st = check_paged(dims, paged)) != GQLA_OK) return st;
+  if (!q_abs || !latent_cache || !w_uv || !o_lat || !out) return fail(GQLA_ERR_INVALID_ARG, "null tensor pointer");
+  const Plan pl = plan(dims, paged, GQLA_PATH_ABSORB);
+  if (!(pl.tuned && gqla::tuned_combine_out_supported(dims, pl.n_split))) {
+    // unsplit (the decode writes o_lat itself) or shapes without the fused kernel
+    if ((st = gqla_decode_absorb(dims, paged, q_abs, latent_cache, workspace, workspace_bytes, o_lat, lse, stream)) !=
+        GQLA_OK)
+      return st;
+    return gqla_out_proj(dims, o_lat, w_uv, out, stream);
+  }
+  if ((st = run_decode(dims, paged, GQLA_PATH_ABSORB, q_abs, latent_cache, workspace, workspace_bytes, o_lat,
+                       gqla::OUT_F32, lse, stream, true)) != GQLA_OK)
+    return st;
+  const size_t rows = static_cast<size_t>(dims->batch) * dims->s_q * dims->num_heads;
+  const float* ws_o = static_cast<const float*>(workspace);
+  const float* ws_lse = ws_o + rows * pl.n_split * dims->latent_rank;
+  hipError_t e = gqla::launch_tuned_combine_out(proj_params(dims), ws_o, ws_lse, pl.n_split, o_lat, lse, w_uv, out,
+                                                static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GQLA_OK : hip_fail(e, "fused combine and value projection launch");
 }
 
 gqla_status gqla_out_proj(const gqla_dims* dims, const float* o_lat, const void* w_uv, void* out,

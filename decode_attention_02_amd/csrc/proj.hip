@@ -216,7 +216,186 @@ __global__ __launch_bounds__(64) void out_proj_kernel(ProjParams d, const float*
   }
 }
 
+// Split combine fused with the value projection (absorb path, split decode). Workgroup
+// (row tile of R rows of group g, g) merges its rows' split partials,
+//   o = sum_s w_s o_s / sum_s w_s,  w_s = exp(lse_s - max lse),
+// writes them to o_lat (and lse), keeps them in LDS as bf16 high and low parts, and applies
+// W_UV^g to them: wave w takes W_UV^g rows 32w .. +32 (two 16-row MFMA tiles, A from global
+// memory) against the 16 MFMA columns (B from LDS; columns R .. 15 are zero when R < 16).
+// One launch instead of the combine and the value projection, and the merged rows are read
+// back from LDS instead of memory. R < 16 gives small batches enough workgroups: the merge
+// is a latency-bound read of the partials, and 64 workgroups leave most CUs idle.
+constexpr int kCombMaxSplits = 64;
+constexpr int kCombPad = kDC + 8;   // LDS row stride in bf16: rows start 16 bytes apart in the banks
+
+template <int R>
+__global__ __launch_bounds__(256) void combine_out_proj_kernel(ProjParams d, const float* ws_o, const float* ws_lse,
+                                                               int n_split, float* o_lat, float* lse_out,
+                                                               const bf16_t* w_uv, bf16_t* out) {
+  constexpr int T = 256 / R;       // threads per row
+  constexpr int C = kDC / 4 / T;   // float4 columns per thread and split
+  constexpr int U = 16 / C;        // splits per pass: 16 float4 loads in flight per thread
+  static_assert(R == 4 || R == 8 || R == 16, "row tile");
+  __shared__ float s_w[R][kCombMaxSplits];
+  __shared__ float s_inv[R];
+  __shared__ __attribute__((aligned(16))) bf16_t s_hi[16][kCombPad];
+  __shared__ __attribute__((aligned(16))) bf16_t s_lo[16][kCombPad];
+  const int g = blockIdx.y;
+  const int gs = d.H / d.G;
+  const int rows_g = d.rows * gs;
+  const int rg0 = blockIdx.x * R;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = tid / T, j = tid % T;
+  const int rg = rg0 + r;
+  const bool live = rg < rows_g;
+  const int64_t row = live ? group_row(rg, g, gs, d.H) : 0;
+  // This wave's 32 rows of W_UV^g as MFMA A operands (wave w, rows 32 w + 16 t + col, 8
+  // latent values from 32 ks + 8 grp), loaded first so that they arrive under the merge.
+  const int col = lane & 15, grp = lane >> 4;
+  bf16x8 wa[kDC / 32][2];
+  {
+    const bf16_t* wsrc = w_uv + (static_cast<int64_t>(g) * kDV + 32 * wave + col) * kDC + 8 * grp;
+#pragma unroll
+    for (int ks = 0; ks < kDC / 32; ++ks)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) wa[ks][t] = *reinterpret_cast<const bf16x8*>(wsrc + 16 * t * kDC + 32 * ks);
+  }
+  // Weights: T threads per row, each over every T-th split, then a reduction over the T.
+  {
+    const float* lse = ws_lse + row * n_split;
+    float m = -INFINITY;
+    bool nan = false;
+    for (int sp = j; sp < n_split; sp += T) {
+      const float l = live ? lse[sp] : -INFINITY;
+      nan |= l != l;
+      m = fmaxf(m, l);
+    }
+    for (int o = T / 2; o > 0; o >>= 1) {
+      m = fmaxf(m, __shfl_xor(m, o, T));
+      nan |= __shfl_xor(static_cast<int>(nan), o, T) != 0;
+    }
+    float tot = 0.f;
+    for (int sp = j; sp < n_split; sp += T) {
+      const float l = live ? lse[sp] : -INFINITY;
+      const float w = (l == -INFINITY) ? 0.f : expf(l - m);
+      s_w[r][sp] = w;
+      tot += w;
+    }
+    for (int o = T / 2; o > 0; o >>= 1) tot += __shfl_xor(tot, o, T);
+    const bool nan_row = nan || !(tot > 0.f);
+    if (j == 0) {
+      s_inv[r] = live ? (nan_row ? nan_f32() : 1.f / tot) : 0.f;
+      if (live && lse_out != nullptr) lse_out[row] = nan_row ? nan_f32() : m + logf(tot);
+    }
+  }
+  if constexpr (R < 16) {   // the unused MFMA columns
+    for (int i = tid; i < (16 - R) * kCombPad / 8; i += 256) {
+      const int rr = R + i / (kCombPad / 8), c = 8 * (i % (kCombPad / 8));
+      *reinterpret_cast<uint4*>(&s_hi[rr][c]) = make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4*>(&s_lo[rr][c]) = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  __syncthreads();
+  // Merge: thread (row r, j) takes the float4 columns j + T k (k < C) of the row's 512
+  // features, so the T threads of a row read 16 T contiguous bytes per k. U splits per
+  // pass, their loads issued before the first product, so a thread waits about once per
+  // U splits instead of once per split.
+  {
+    const float* src = ws_o + row * n_split * kDC;
+    float4 acc[C];
+#pragma unroll
+    for (int k = 0; k < C; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (live) {
+      for (int sp0 = 0; sp0 < n_split; sp0 += U) {
+        float w[U];
+        float4 v[U][C];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          w[u] = sp0 + u < n_split ? s_w[r][sp0 + u] : 0.f;
+          const float* o = src + static_cast<int64_t>(sp0 + u) * kDC;
+          // an empty split (weight 0, uniform over the row): its partials are not read
+#pragma unroll
+          for (int k = 0; k < C; ++k)
+            v[u][k] = w[u] != 0.f ? *reinterpret_cast<const float4*>(o + 4 * (j + T * k)) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int k = 0; k < C; ++k) {
+            acc[k].x += w[u] * v[u][k].x; acc[k].y += w[u] * v[u][k].y;
+            acc[k].z += w[u] * v[u][k].z; acc[k].w += w[u] * v[u][k].w;
+          }
+      }
+    }
+    const float inv = s_inv[r];
+#pragma unroll
+    for (int k = 0; k < C; ++k) {
+      const int f = 4 * (j + T * k);   // first of the 4 features
+      const float x[4] = {acc[k].x * inv, acc[k].y * inv, acc[k].z * inv, acc[k].w * inv};
+      if (live) *reinterpret_cast<float4*>(o_lat + row * kDC + f) = make_float4(x[0], x[1], x[2], x[3]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const __bf16 h = static_cast<__bf16>(x[e]);
+        s_hi[r][f + e] = __builtin_bit_cast(bf16_t, h);
+        s_lo[r][f + e] = __builtin_bit_cast(bf16_t, static_cast<__bf16>(x[e] - static_cast<float>(h)));
+      }
+    }
+  }
+  __syncthreads();
+  // out^T = W_UV^g o^T: B = 8 latent values of row col.
+  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int ks = 0; ks < kDC / 32; ++ks) {
+    const bf16x8 hi = *reinterpret_cast<const bf16x8*>(&s_hi[col][32 * ks + 8 * grp]);
+    const bf16x8 lo = *reinterpret_cast<const bf16x8*>(&s_lo[col][32 * ks + 8 * grp]);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ks][t], hi, acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ks][t], lo, acc[t], 0, 0, 0);
+    }
+  }
+  const int rgc = rg0 + col;
+  if (col < R && rgc < rows_g) {
+    const int64_t orow = group_row(rgc, g, gs, d.H);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      bf16_t packed[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) packed[k] = f32_to_bf16(acc[t][k]);
+      *reinterpret_cast<uint2*>(out + orow * kDV + 32 * wave + 16 * t + 4 * grp) = *reinterpret_cast<uint2*>(packed);
+    }
+  }
+}
+
+// Row tile of the fused combine: the largest of 16, 8, 4 rows that still gives at least
+// 256 workgroups (one per CU), else 4.
+int comb_rows(int rows_g, int G) {
+  for (int R = 16; R > 4; R /= 2)
+    if (static_cast<int64_t>((rows_g + R - 1) / R) * G >= 256) return R;
+  return 4;
+}
+
 }  // namespace
+
+bool tuned_combine_out_supported(const gqla_dims* d, int n_split) {
+  return d->dtype == GQLA_BF16 && d->latent_rank == kDC && d->v_dim == kDV && n_split > 1 && n_split <= kCombMaxSplits;
+}
+
+hipError_t launch_tuned_combine_out(const ProjParams& p, const float* ws_o, const float* ws_lse, int n_split,
+                                    float* o_lat, float* lse, const void* w_uv, void* out, hipStream_t s) {
+  const int rows_g = p.rows * (p.H / p.G);
+  const int R = comb_rows(rows_g, p.G);
+  const dim3 grid((rows_g + R - 1) / R, p.G);
+  const bf16_t* wv = static_cast<const bf16_t*>(w_uv);
+  bf16_t* o = static_cast<bf16_t*>(out);
+  if (R == 16)
+    combine_out_proj_kernel<16><<<grid, 256, 0, s>>>(p, ws_o, ws_lse, n_split, o_lat, lse, wv, o);
+  else if (R == 8)
+    combine_out_proj_kernel<8><<<grid, 256, 0, s>>>(p, ws_o, ws_lse, n_split, o_lat, lse, wv, o);
+  else
+    combine_out_proj_kernel<4><<<grid, 256, 0, s>>>(p, ws_o, ws_lse, n_split, o_lat, lse, wv, o);
+  return hipGetLastError();
+}
 
 bool tuned_absorb_query_supported(const gqla_dims* d) {
   return d->dtype == GQLA_BF16 && d->latent_rank == kDC && d->rope_dim == kDR &&

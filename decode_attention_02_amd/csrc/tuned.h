@@ -26,6 +26,11 @@ hipError_t launch_tuned_absorb_query(const ProjParams& p, const void* q_nope, co
 bool tuned_out_proj_supported(const gqla_dims* d);
 hipError_t launch_tuned_out_proj(const ProjParams& p, const float* o_lat, const void* w_uv, void* out,
                                  hipStream_t s);
+// Split combine fused with the value projection (absorb path): d_c = 512, d_v = 128, bf16,
+// 2..64 splits.
+bool tuned_combine_out_supported(const gqla_dims* d, int n_split);
+hipError_t launch_tuned_combine_out(const ProjParams& p, const float* ws_o, const float* ws_lse, int n_split,
+                                    float* o_lat, float* lse, const void* w_uv, void* out, hipStream_t s);
 bool tuned_expand_supported(const gqla_dims* d);
 hipError_t launch_tuned_expand(const ProjParams& p, const void* latent, const void* w_uk, const void* w_uv,
                                const int32_t* block_ids, int64_t n_blocks, int64_t num_blocks,

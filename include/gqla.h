@@ -171,6 +171,21 @@ gqla_status gqla_out_proj(const gqla_dims* dims, const float* o_lat, const void*
                           void* out, void* stream);
 
 /*
+ * gqla_decode_absorb_out — gqla_decode_absorb followed by gqla_out_proj, in one call (steps 2
+ * and 3 of the MQA-absorb path). When the decode is split, the split combine and the W_UV^g
+ * product run as one kernel that keeps the merged latent rows on chip; unsplit, or at shapes
+ * without that kernel, it is exactly the two calls.
+ *   q_abs, latent_cache, workspace, lse : as gqla_decode_absorb (same workspace size)
+ *   w_uv  : data [G][d_v][d_c]
+ *   o_lat : fp32 [B][s_q][H][d_c]  (output; the latent rows are written on every form)
+ *   out   : data [B][s_q][H][d_v]  (output)
+ * Errors: those of gqla_decode_absorb and gqla_out_proj.
+ */
+gqla_status gqla_decode_absorb_out(const gqla_dims* dims, const gqla_paged* paged, const void* q_abs,
+                                   const void* latent_cache, const void* w_uv, void* workspace,
+                                   size_t workspace_bytes, float* o_lat, void* out, float* lse, void* stream);
+
+/*
  * gqla_expand_cache — expand latent blocks into the per-group K/V cache (GQA path).
  * For each listed block p, group g and slot r (gqla_attn.py docstring: the latent is
  * expanded into num_groups full key/value heads):

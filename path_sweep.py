@@ -2,7 +2,7 @@
 
 For each workload and query-row count it times, on random data of the workload's shape
 (batch, context lengths, paging), the two GQLA decode paths as a serving step runs them:
-  absorb: gqla_absorb_query -> gqla_decode_absorb (+ split combine) -> gqla_out_proj
+  absorb: gqla_absorb_query -> gqla_decode_absorb_out (decode; split combine fused with W_UV^g)
   GQA:    gqla_decode_gqa (+ split combine) over an expanded cache that is already resident
 and, separately, the per-token cost of the append path (gqla_append_tokens of the s_q new
 tokens of every sequence, latent rows + RoPE + their expansion into the groups) and the
@@ -146,8 +146,7 @@ def run_workload(name, reps, gen, flush, rope_shared=1):
 
         def absorb():
             L.gqla_absorb_query(d, q_nope, q_rope, w_uk, q_abs)
-            L.gqla_decode_absorb(d, paged, q_abs, latent, wsa, o_lat)
-            L.gqla_out_proj(d, o_lat, w_uv, out)
+            L.gqla_decode_absorb_out(d, paged, q_abs, latent, w_uv, wsa, o_lat, out)
 
         t_med, t_best = _time(absorb, reps, flush)
         kv = float(ctx.sum()) * dq * elt

@@ -62,6 +62,9 @@ def test_invalid_dims_rejected_before_launch(bad, msg):
     assert _lib.LIB.gqla_absorb_query(ctypes.byref(d), 1, 1, 1, 1, None) == _lib.GQLA_ERR_INVALID_ARG
     assert _lib.LIB.gqla_out_proj(ctypes.byref(d), 1, 1, 1, None) == _lib.GQLA_ERR_INVALID_ARG
     assert _lib.LIB.gqla_expand_cache(ctypes.byref(d), 1, 1, 1, 1, 1, 1, 1, None) == _lib.GQLA_ERR_INVALID_ARG
+    p = _lib.gqla_paged(1, 1, 128, 8192, 4096, 0)
+    assert _lib.LIB.gqla_decode_absorb_out(ctypes.byref(d), ctypes.byref(p), 1, 1, 1, 1, 1 << 30, 1, 1, None,
+                                           None) == _lib.GQLA_ERR_INVALID_ARG
 
 
 def test_invalid_paging_and_path_rejected():
@@ -80,9 +83,18 @@ def test_invalid_paging_and_path_rejected():
         == _lib.GQLA_ERR_INVALID_ARG
     assert _lib.LIB.gqla_decode_absorb(ctypes.byref(dc), None, 1, 1, None, 0, 1, None, None) \
         == _lib.GQLA_ERR_INVALID_ARG
+    assert _lib.LIB.gqla_decode_absorb_out(ctypes.byref(dc), None, 1, 1, 1, 1, 1 << 30, 1, 1, None, None) \
+        == _lib.GQLA_ERR_INVALID_ARG
     # null tensors
     assert _lib.LIB.gqla_absorb_query(ctypes.byref(dc), None, 1, 1, 1, None) == _lib.GQLA_ERR_INVALID_ARG
     assert b"null" in _lib.LIB.gqla_last_error()
+    pv = _lib.gqla_paged(1, 1, 128, 8192, 4096, 0)
+    for nulled in range(5):   # q_abs, latent_cache, w_uv, o_lat, out
+        args = [1, 1, 1, 1, 1 << 30, 1, 1]
+        args[[0, 1, 2, 5, 6][nulled]] = None
+        assert _lib.LIB.gqla_decode_absorb_out(ctypes.byref(dc), ctypes.byref(pv), *args, None, None) \
+            == _lib.GQLA_ERR_INVALID_ARG
+        assert b"null" in _lib.LIB.gqla_last_error()
     # zero blocks to expand is a no-op, negative is an error
     assert _lib.LIB.gqla_expand_cache(ctypes.byref(dc), None, None, None, None, 0, 1, None, None) == 0
     assert _lib.LIB.gqla_expand_cache(ctypes.byref(dc), 1, 1, 1, 1, -1, 1, 1, None) == _lib.GQLA_ERR_INVALID_ARG
@@ -92,6 +104,10 @@ def test_workspace_too_small_rejected_before_launch():
     d = _dims().c()
     p = _lib.gqla_paged(1, 1, 128, 8192, 4096, 4)
     st = _lib.LIB.gqla_decode_gqa(ctypes.byref(d), ctypes.byref(p), 1, 1, 1, 16, 1, None, None)
+    assert st == _lib.GQLA_ERR_WORKSPACE
+    # the fused absorb entry point checks the same workspace before its first launch
+    ds = _dims(dtype=G.GQLA_BF16).c()
+    st = _lib.LIB.gqla_decode_absorb_out(ctypes.byref(ds), ctypes.byref(p), 1, 1, 1, 1, 16, 1, 1, None, None)
     assert st == _lib.GQLA_ERR_WORKSPACE
 
 
