@@ -154,7 +154,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // latent values and B = 32 latent values x 16 tokens, both read straight from global
 // memory with every load of the wave in flight at once. The workgroups z = nz rotate the
 // tile's keys, write the latent rows (group 0) and copy the keys into K, so that neither
-// kind waits for the other's memory round trips (the step is latency-bound).
+// kind waits for the other's memory round trips (the step is latency-bound). With no
+// expanded cache (the absorb path keeps only the latent) the grid is just those workgroups.
 template <int DC>
 __global__ __launch_bounds__(256) void append_tokens_mfma(AppendParams a, const bf16_t* c_new, const bf16_t* kr_new,
                                                           const bf16_t* w_uk, const bf16_t* w_uv, bf16_t* latent,
@@ -244,15 +245,17 @@ __global__ __launch_bounds__(256) void append_tokens_mfma(AppendParams a, const 
       const int j = idx / a.dr, k = idx % a.dr;
       const int64_t dst = s_dst[j];
       if (dst < 0) continue;
-      const int64_t id = dst / kBlock;
-      const int s = static_cast<int>(dst % kBlock);
-      bf16_t* blk = expanded + id * lay.block;
-      if (!a.rope_shared) {   // into this group's K
-        const int f = a.dn + k, sl = f / kSlab, w = min(kSlab, lay.k_feats - sl * kSlab);
-        blk[lay.rope + g * lay.chunk + static_cast<int64_t>(sl) * kBlock * kSlab + s * w + f % kSlab] = s_rope[idx];
-      } else if (g == 0) {    // once, into the block's shared key area
-        const int sl = k / kSlab, w = min(kSlab, a.dr - sl * kSlab);
-        blk[static_cast<int64_t>(sl) * kBlock * kSlab + s * w + k % kSlab] = s_rope[idx];
+      if (expanded != nullptr) {
+        const int64_t id = dst / kBlock;
+        const int s = static_cast<int>(dst % kBlock);
+        bf16_t* blk = expanded + id * lay.block;
+        if (!a.rope_shared) {   // into this group's K
+          const int f = a.dn + k, sl = f / kSlab, w = min(kSlab, lay.k_feats - sl * kSlab);
+          blk[lay.rope + g * lay.chunk + static_cast<int64_t>(sl) * kBlock * kSlab + s * w + f % kSlab] = s_rope[idx];
+        } else if (g == 0) {    // once, into the block's shared key area
+          const int sl = k / kSlab, w = min(kSlab, a.dr - sl * kSlab);
+          blk[static_cast<int64_t>(sl) * kBlock * kSlab + s * w + k % kSlab] = s_rope[idx];
+        }
       }
       if (write_latent) latent[dst * dq + DC + k] = s_rope[idx];
     }
@@ -287,9 +290,10 @@ __global__ __launch_bounds__(256) void append_tokens_mfma(AppendParams a, const 
 hipError_t launch_append(const AppendParams& a, const void* c_new, const void* kr_new, const void* w_uk,
                          const void* w_uv, void* latent, void* expanded, bool bf16, hipStream_t s) {
   const int tiles = (a.n_tok + kAppendTile - 1) / kAppendTile;
-  if (bf16 && expanded != nullptr && a.dc == 512 && a.dr <= 128 && (a.dn + a.dv) % 16 == 0) {
-    const int nz = (a.dn + a.dv + 63) / 64;
-    dim3 grid(tiles, a.G, nz + 1);
+  if (bf16 && a.dc == 512 && a.dr <= 128 && (a.dn + a.dv) % 16 == 0) {
+    // Without an expanded cache only the rotation / latent-copy workgroups run (nz = 0).
+    const int nz = expanded != nullptr ? (a.dn + a.dv + 63) / 64 : 0;
+    dim3 grid(tiles, expanded != nullptr ? a.G : 1, nz + 1);
     append_tokens_mfma<512><<<grid, 256, 0, s>>>(a, static_cast<const bf16_t*>(c_new), static_cast<const bf16_t*>(kr_new),
                                                  static_cast<const bf16_t*>(w_uk), static_cast<const bf16_t*>(w_uv),
                                                  static_cast<bf16_t*>(latent), static_cast<bf16_t*>(expanded), nz);

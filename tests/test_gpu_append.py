@@ -154,3 +154,28 @@ def test_append_without_latent_cache_writes_the_same_expanded_cache(name, dtype,
     assert np.array_equal(_bits(expanded), _bits(exp_only))
     with pytest.raises(run.G.GqlaError):
         run.G.gqla_append_tokens(run.dims, run.paged, c_new, kr_new, THETA, run.w_uk, run.w_uv, None, None)
+
+
+@pytest.mark.parametrize("name,dtype,s_q,ctx", [
+    ("tiny-fp32", "f32", 2, [2, 64, 65, 100]),
+    ("llama3-8b-b32-ctx8k", "bf16", 1, [1, 63, 64, 65, 129, 700, 3, 90, 191, 257, 1000, 8192, 4, 5, 6, 7, 8, 9]),
+    ("dsv3-b64-ctx8k", "bf16", 2, [2, 64, 65, 127, 1500]),
+])
+def test_append_without_expanded_cache_writes_the_same_latent_cache(name, dtype, s_q, ctx):
+    """The absorb path keeps no expanded cache: the latent rows must come out bit-identical to
+    the append that also expands them."""
+    w = workload(name)
+    x = generate(w, s_q, batch=len(ctx), ctx_lens=ctx, dtype=dtype, shuffled=True, extra_blocks=2)
+    run = Run(x, 0)
+    expanded = run.expand()
+    lat_only = run.cache.clone()
+    before = _bits(run.cache)
+    rng = np.random.default_rng(22)
+    c_new = to_dev(_store(rng.standard_normal((len(ctx), s_q, w.latent)), dtype), dtype)
+    kr_new = to_dev(_store(rng.standard_normal((len(ctx), s_q, w.rope)), dtype), dtype)
+    log(f"append without expanded cache {name} {dtype} s_q={s_q}")
+    run.G.gqla_append_tokens(run.dims, run.paged, c_new, kr_new, THETA, run.w_uk, run.w_uv, run.cache, expanded)
+    run.G.gqla_append_tokens(run.dims, run.paged, c_new, kr_new, THETA, run.w_uk, run.w_uv, lat_only, None)
+    torch.cuda.synchronize()
+    assert not np.array_equal(_bits(run.cache), before)
+    assert np.array_equal(_bits(run.cache), _bits(lat_only))
