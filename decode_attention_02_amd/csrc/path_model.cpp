@@ -29,7 +29,7 @@ struct Mi355xRates {
   double absorb_mfma = 0.8e15;    // absorb decode when MFMA/LDS-bound, flop/s
   double absorb_fixed_us = 15.0;  // absorb decode fixed cost
   double gqa_bw = 6.8e12;         // GQA decode expanded-cache streaming, B/s (per-group layout)
-  double gqa_shared_bw = 6.6e12;  // same, RoPE key once per block
+  double gqa_shared_bw = 7.0e12;  // same, RoPE key once per block
   double gqa_fixed_us = 20.0;     // GQA step fixed cost (decode and new-token expansion)
   double gqa_mfma = 1.0e15;       // GQA decode padded MFMA work, flop/s
   double expand_mfma = 0.35e15;   // cache expansion, flop/s
@@ -50,12 +50,13 @@ PathEstimate estimate_paths(const gqla_dims* d, int64_t total_ctx, int n_split_a
   const double rows = B * s * H;
   auto us = [](double x) { return x * 1e6; };
 
-  // MQA-absorb: absorbed query, latent decode, (combine), value projection.
+  // MQA-absorb: absorbed query, latent decode, value projection (split: one kernel that
+  // merges the partials and applies W_UV^g, as gqla_decode_absorb_out runs it).
   const double abs_bytes = tok * (dc + dr) * elt;
   const double abs_flops = vis * H * 2.0 * (2.0 * dc + dr);
   double t_abs = std::max(us(abs_bytes / r.absorb_bw), us(abs_flops / r.absorb_mfma)) + r.absorb_fixed_us;
   t_abs += 2 * r.launch_us + us(rows * dn * dc * 2.0 / r.proj_mfma) + us(rows * dc * dv * 4.0 / r.proj_mfma);
-  if (n_split_abs > 1) t_abs += r.launch_us + us(rows * n_split_abs * dc * 4.0 / r.combine_bw);
+  if (n_split_abs > 1) t_abs += us(rows * n_split_abs * dc * 4.0 / r.combine_bw);
 
   // GQA: expansion of the blocks holding the new tokens, grouped decode, (combine).
   const double gqa_bytes = tok * (d->rope_shared ? G * (dn + dv) + dr : G * (dqk + dv)) * elt;
