@@ -66,3 +66,69 @@ def test_plain_c_program_links_and_calls_the_abi(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "c caller ok" in r.stdout
+
+
+# The same caller against a build of the host side (argument checks, planning, the path
+# model) with AddressSanitizer, so that an out-of-bounds access in the library's host code
+# stops the program. The kernels' objects are linked uninstrumented; no call here reaches a
+# device. A second program passes one float where gqla_pick_path writes two, and must be
+# stopped: it shows that an overrun inside the library is caught.
+OVERRUN = r"""
+#include <string.h>
+#include "gqla.h"
+int main(void) {
+  gqla_dims d;
+  int32_t path = -1;
+  float est = 0.f;
+  memset(&d, 0, sizeof d);
+  d.batch = 32; d.num_heads = 32; d.num_groups = 8; d.latent_rank = 512; d.rope_dim = 64;
+  d.nope_dim = 64; d.v_dim = 128; d.s_q = 1; d.block_size = 64; d.dtype = GQLA_BF16;
+  return gqla_pick_path(&d, (int64_t)32 * 8192, 8192, &path, &est) == GQLA_OK ? 0 : 3;
+}
+"""
+
+
+def _asan_runtime():
+    import glob
+    libs = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return libs[-1] if libs else None
+
+
+@pytest.mark.skipif(not os.path.exists("/opt/rocm/llvm/bin/clang") or _asan_runtime() is None,
+                    reason="needs ROCm's clang and its AddressSanitizer runtime")
+def test_c_caller_with_host_code_under_address_sanitizer(tmp_path):
+    from decode_attention_02_amd import build as B
+    host_srcs = ["gqla_api.cpp", "path_model.cpp"]
+    kernel_objs = [os.path.join(B.BUILD, os.path.basename(s) + ".o") for s in B.sources()
+                   if os.path.basename(s) not in host_srcs]
+    if not all(os.path.exists(o) for o in kernel_objs):
+        pytest.skip("build the library first (its kernel objects are linked as they are)")
+    objs = []
+    for name in host_srcs:
+        obj = str(tmp_path / (name + ".o"))
+        cmd = [B.hipcc()] + B.COMMON + ["-O1", "-g", "-Xarch_host", "-fsanitize=address",
+                                        "-Xarch_host", "-fno-omit-frame-pointer",
+                                        "-c", os.path.join(B.CSRC, name), "-o", obj]
+        subprocess.run(cmd, check=True, capture_output=True, text=True)
+        objs.append(obj)
+    lib = tmp_path / "libgqla.so"
+    link = [B.hipcc(), f"--offload-arch={B.ARCH}", "-shared", "-fPIC", "-o", str(lib)] + objs + kernel_objs + \
+        ["-Xarch_host", "-fsanitize=address", "-shared-libasan"]
+    subprocess.run(link, check=True, capture_output=True, text=True)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0",
+               LD_LIBRARY_PATH=os.path.dirname(_asan_runtime()) + ":" + os.environ.get("LD_LIBRARY_PATH", ""))
+    results = {}
+    for name, text in (("caller", PROGRAM), ("overrun", OVERRUN)):
+        src = tmp_path / f"{name}.c"
+        src.write_text(text)
+        exe = tmp_path / name
+        cc = ["/opt/rocm/llvm/bin/clang", "-std=c11", "-g", "-fno-omit-frame-pointer", "-shared-libasan",
+              "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe), "-L", str(tmp_path), "-lgqla",
+              f"-Wl,-rpath,{tmp_path}"]
+        cc.insert(3, "-fsanitize" + "=address")
+        subprocess.run(cc, check=True, capture_output=True, text=True)
+        results[name] = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120, env=env)
+    ok = results["caller"]
+    assert ok.returncode == 0 and "c caller ok" in ok.stdout, ok.stdout + ok.stderr
+    bad = results["overrun"]
+    assert bad.returncode != 0 and "stack-buffer-overflow" in bad.stderr, bad.stderr[-2000:]
