@@ -5,10 +5,10 @@
 // absorbed form, which GQLA keeps unchanged: "GQLA: Attention latente ...", English
 // abstract; gqla_attn.py docstring: a single MQA-style head per layer).
 //
-// All H * s_q query rows of a sequence read the same 64-token latent tiles, so the
-// tile is fetched from HBM once per workgroup and shared through LDS:
-//   * tiles (64 tokens x 576 bf16 = 72 KiB) are copied global -> LDS by
-//     global_load_lds_dwordx4 (no register staging), double-buffered, with an XOR
+// All H * s_q query rows of a sequence read the same latent tiles, so a tile is fetched
+// from HBM once per workgroup and shared through LDS:
+//   * tiles (64 tokens x 576 bf16 = 72 KiB, or 32-token sub-tiles) are copied
+//     global -> LDS by global_load_lds_dwordx4 (no register staging), with an XOR
 //     swizzle of the 16-byte chunks inside each 128-byte group so that both LDS
 //     access patterns below are bank-conflict free;
 //   * scores S^T = C Q^T (v_mfma_f32_16x16x32_bf16, A = 16 tokens x 32 latent features
@@ -16,15 +16,16 @@
 //   * the value product O^T = C^T P^T needs the latent with tokens along the
 //     contraction, which ds_read_b64_tr_b16 delivers directly from the row-major tile;
 //     P is the B operand;
-//   * 16 or 32 rows (AbsorbCta): each wave owns 16 query rows for both products and
-//     each tile's two 32-token halves go to two waves, merged at the end, so a
-//     workgroup still has 4 waves streaming;
-//   * 64 rows and more (AbsorbQuadCta): 64 rows per workgroup, the score product split
-//     over (32-row group, token half) and the value product over latent-feature
-//     quarters, with P exchanged through LDS, so each operand read feeds two (scores)
-//     or four (values) MFMAs; 128 to 512 rows use 2 to 8 such workgroups per
-//     (sequence, split), placed on the same XCD so the repeated tile reads are served
-//     from that XCD's L2.
+//   * 16 or 32 rows (AbsorbCta, bound by HBM): each wave owns 16 query rows for both
+//     products and each double-buffered tile's two 32-token halves go to two waves,
+//     merged at the end, so a workgroup still has 4 waves streaming;
+//   * 64 rows and more (AbsorbSpecCta, bound by the matrix cores): 64 rows per
+//     workgroup of eight waves, four forming scores and P (two row tiles and one
+//     16-token half each, so each operand read feeds two MFMAs) and four applying P to a
+//     quarter of the latent features of all rows (each transposed read feeding four
+//     MFMAs), one 32-token sub-tile apart, with P exchanged through LDS; 128 to 512 rows
+//     use 2 to 8 such workgroups per (sequence, split), placed on the same XCD so the
+//     repeated tile reads are served from that XCD's L2.
 #include "device_common.h"
 #include "gqla_internal.h"
 #include "tuned.h"
@@ -508,148 +509,280 @@ hipError_t launch(const AttnParams& p, int parts, hipStream_t s) {
   return hipGetLastError();
 }
 
-// P^T operands of all four row tiles (2 token halves x 64 lanes x 16 bytes each) and the
-// reference maxima their producers used (per row tile, half and row).
-constexpr int kQuadP = 4 * 2 * 1024;
-__shared__ __attribute__((aligned(16))) char g_qx[kQuadP + 4 * 2 * 16 * 4];
+// ---------------------------------------------------------------------------------------
+// 64 rows per workgroup with the two products on different waves: eight waves, two per
+// SIMD, waves 0-3 forming scores and P, waves 4-7 applying P to the latent. The latent
+// streams in 32-token sub-tiles through a ring of four LDS slots; iteration i:
+//   * score wave (sg, th) forms S^T for rows 32 sg .. +32 (two row tiles, each operand read
+//     feeding two MFMAs) over tokens 16 th .. +16 of sub-tile i, its online softmax against
+//     its own running reference, and publishes P^T and that reference through LDS;
+//   * value wave v copies sub-tile i + 2 into the free slot, zeroes the rows of sub-tile i
+//     past the context, and applies P of sub-tile i - 1 to latent features 128 v .. +128 of
+//     all four row tiles (each transposed read feeding four MFMAs), first raising its own
+//     reference to the larger published one and rescaling what was formed against less.
+// One barrier per iteration. The two waves of a SIMD have different roles, so one's
+// exponentials and LDS waits run under the other's matrix work; each role keeps only its
+// own state (queries or accumulators) within 256 registers.
+constexpr int kSubTok = 32;
+constexpr int kSubBytes = kSubTok * kRowBytes;    // 36864
+constexpr int kSubCopies = kSubBytes / 1024;      // 1 KiB copies per sub-tile (36)
+__shared__ __attribute__((aligned(16))) char g_sub0[kSubBytes];
+__shared__ __attribute__((aligned(16))) char g_sub1[kSubBytes];
+__shared__ __attribute__((aligned(16))) char g_sub2[kSubBytes];
+__shared__ __attribute__((aligned(16))) char g_sub3[kSubBytes];
+__shared__ __attribute__((aligned(16))) char g_sp[2][4 * 64 * 16];   // P^T operands [buf][row tile][lane]
+__shared__ float g_sm[2][4][2][16];   // reference of each published P [buf][row tile][th][row]
+__shared__ float g_sl[4][2][16];      // final row sums of the score waves [row tile][th][row]
+__shared__ float g_sr[4][2][16];      // and their final references
 
-// 64 rows per workgroup, four waves, no wave holding more than it must:
-//   * scores: wave w takes row tiles 2*(w/2), 2*(w/2)+1 (32 rows of queries in registers)
-//     over token half w%2 of the tile, so each operand read feeds two MFMAs and each wave
-//     reads half the tile;
-//   * values: wave w takes latent features 128*w .. +128 for all four row tiles and both
-//     halves, so each transposed read feeds four MFMAs and the tile is read transposed
-//     exactly once per workgroup.
-// The P^T operands go through LDS between the two phases. The two waves that score the
-// same rows see different tokens and so different maxima; instead of agreeing on a
-// maximum before the exponentials (a second barrier per tile), each uses its own
-// reference, raised only when its scores pass the agreed one by more than 2^8, and
-// publishes it with P. After the exchange every wave takes the larger of the two per row
-// as the new agreed reference and rescales what was computed against a smaller one (the
-// accumulator, the other half's P, a score wave's row sums), a branch that is only taken
-// when some reference grew.
-struct AbsorbQuadCta {
-  static constexpr int W = 4;
-  static constexpr int NT = 4;                                 // row tiles
-  static constexpr int PER_WAVE = kChunks * kBlock / 64 / W;   // 1 KiB copies per wave per tile (18)
-  static constexpr int FQ = kDC / 16 / W;                      // feature tiles per wave (8)
-  static constexpr int KS = kDQ / 32;                          // k-steps of the score product (18)
-  static constexpr int NS = 2 * KS;                            // score operand reads per wave per tile
-  static constexpr int SB = 2;                                 // score reads per batch
-  static constexpr int VB = 4;                                 // value feature tiles per batch
-  static_assert(NS % SB == 0 && FQ % VB == 0, "batches");
-  static_assert(NS % PER_WAVE == 0, "copies spread evenly over the score reads");
-  static_assert((PER_WAVE * 64) % (16 * kChunks) == 0, "wave copy block must hold whole swizzle periods");
+template <int S>
+__device__ __forceinline__ char* sub_buf() {
+  return S == 0 ? g_sub0 : S == 1 ? g_sub1 : S == 2 ? g_sub2 : g_sub3;
+}
+
+struct AbsorbSpecCta {
+  static constexpr int W = 8;
+  static constexpr int NT = 4;                  // row tiles
+  static constexpr int KS = kDQ / 32;           // k-steps of the score product (18)
+  static constexpr int FQ = kDC / 16 / 4;       // feature tiles per value wave (8)
+  static constexpr int CPW = kSubCopies / 4;    // copies per value wave per sub-tile (9)
+  static constexpr int SB = 9;                  // score operand reads per batch
+  static constexpr int VB = 8;                  // value feature tiles per batch (all of them)
+  static_assert(KS % SB == 0 && FQ % VB == 0, "batches");
+  static_assert(CPW * 4 == kSubCopies, "sub-tile copies split over the value waves");
 
   const AttnParams& p;
-  int lane, wave, sg, th, col, grp;
-  int b, split, part, L, blk_lo, nb;
+  int lane, wave, col, grp;
+  int b, split, part, L, blk_lo, nb, n_sub;
   bool bad;
-  int n_vis[2];           // visible tokens of this lane's rows in the two score tiles
-  bf16x8 qf[2][KS];       // queries of the two score tiles (B operands)
-  f32x4 acc[NT][FQ];      // O^T of every row tile, this wave's features
-  float m_ref[NT];        // agreed reference maximum of row `col` of each tile (log2 domain)
-  float l_part[2];        // row sums of this wave's tokens, its two score tiles (vs m_ref)
-  float qk_scale;
-  int s_base_even, s_base_odd;
-  int v_base[4];
 
-  __device__ AbsorbQuadCta(const AttnParams& p_) : p(p_) {}
+  __device__ AbsorbSpecCta(const AttnParams& p_) : p(p_) {}
 
-  // Start of this wave's share of block k's tile; uniform, so the copies use a scalar
-  // base and a 32-bit per-lane offset.
-  __device__ __forceinline__ const char* tile_src(int k) const {
-    const int32_t id = __builtin_amdgcn_readfirstlane(max(g_ids[k], 0));
-    return static_cast<const char*>(p.kv) + static_cast<int64_t>(id) * kTileBytes + wave * PER_WAVE * 1024;
+  // Block ids of the split into LDS (-1 marks an id outside the pool), then the workgroup
+  // agrees on `bad` and the number of blocks. Every wave runs this once.
+  __device__ __forceinline__ void stage_ids() {
+    const int32_t* table = p.block_table + static_cast<int64_t>(b) * p.max_blocks + blk_lo;
+    constexpr int kIdsPerThread = kMaxSplitBlocks / (W * 64);
+    int32_t idr[kIdsPerThread];
+#pragma unroll
+    for (int u = 0; u < kIdsPerThread; ++u) {
+      const int i = threadIdx.x + u * W * 64;
+      idr[u] = i < nb ? table[i] : 0;
+    }
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");   // ids, queries, the first copies
+#pragma unroll
+    for (int u = 0; u < kIdsPerThread; ++u) {
+      const int i = threadIdx.x + u * W * 64;
+      if (i < nb) g_ids[i] = (idr[u] < 0 || idr[u] >= p.num_blocks) ? -1 : idr[u];
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    lds_barrier();
+    for (int i = 0; i < nb; ++i) bad |= g_ids[i] < 0;
+    nb = bad ? 0 : nb;
+    n_sub = 2 * nb;
   }
-  // Source offset of copy J (slot_source(64 * J + lane)), recomputed at each use: a table
-  // of 18 offsets per lane would not stay in registers next to the queries and accumulators.
-  // Slot 64 * J + lane lies in token row t0 or t0 + 1 of the wave's rows (rows hold 72 slots).
-  template <int J>
-  __device__ __forceinline__ uint32_t copy_off() const {
-    constexpr int C = 64 * J, T0 = C / kChunks, T1 = kChunks * (T0 + 1) - C;
-    const int up = lane >= T1 ? 1 : 0;
-    const int t = T0 + up;
-    const int cp = lane + (C - kChunks * T0) - kChunks * up;
-    uint32_t off = static_cast<uint32_t>(t * kRowBytes + 16 * ((cp & ~7) | ((cp & 7) ^ swz(t))));
-    asm volatile("" : "+v"(off));   // a separate 32-bit operand, so the copy takes a scalar base
-    return off;
-  }
-  template <int BUF, int J>
-  __device__ __forceinline__ void issue_one(const char* src) {
-    copy16_to_lds(src + copy_off<J>(), (lds_void*)(tile_buf<BUF>() + (wave * PER_WAVE + J) * 1024));
-  }
-  template <int BUF, int J = 0>
-  __device__ __forceinline__ void issue_all(const char* src) {
-    if constexpr (J < PER_WAVE) {
-      issue_one<BUF, J>(src);
-      issue_all<BUF, J + 1>(src);
+
+  // ---- score waves ----
+  struct Score {
+    int sg, th;
+    int n_vis[2];
+    bf16x8 qf[2][KS];
+    float m_ref[2], l_part[2];
+    int s_base_even, s_base_odd;
+  };
+
+  template <int SLOT>
+  __device__ __forceinline__ void score_step(Score& st, int i, float qk_scale) {
+    const char* tile = sub_buf<SLOT>() + st.th * 16 * kRowBytes;
+    auto ld = [&](int ks) {
+      return *reinterpret_cast<const bf16x8*>(tile + ((ks & 1) ? st.s_base_odd : st.s_base_even) + 128 * (ks >> 1));
+    };
+    f32x4 s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    bf16x8 a[KS];
+#pragma unroll
+    for (int k = 0; k < SB; ++k) a[k] = ld(k);
+    // The other token half's references of the previous sub-tile, read under the MFMAs.
+    float other[2] = {-INFINITY, -INFINITY};
+    if (i > 0) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) other[j] = g_sm[(i - 1) & 1][2 * st.sg + j][1 - st.th][col];
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) s[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], st.qf[j][ks], s[j], 0, 0, 0);
+      if (ks % SB == 0 && ks + SB < KS) {
+#pragma unroll
+        for (int k = 0; k < SB; ++k) a[ks + SB + k] = ld(ks + SB + k);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // Lane (row col, grp) holds tokens 16 th + 4 grp + r of the sub-tile, r = 0..3.
+    const int tb = blk_lo * kBlock + i * kSubTok + 16 * st.th + 4 * grp;
+    char* pbuf = g_sp[i & 1];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int t = 2 * st.sg + j;
+      // Adopt the other token half's reference from the previous sub-tile when larger, so
+      // that both halves publish P against the same reference and the value waves rarely
+      // have to rescale it.
+      if (other[j] > st.m_ref[j]) {
+        if (st.m_ref[j] != -INFINITY) st.l_part[j] *= __builtin_amdgcn_exp2f(st.m_ref[j] - other[j]);
+        st.m_ref[j] = other[j];
+      }
+      float sc[4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sc[r] = (tb + r < st.n_vis[j]) ? s[j][r] * qk_scale : -INFINITY;
+        mx = fmaxf(mx, sc[r]);
+      }
+      mx = xor_max(mx);
+      if (mx > st.m_ref[j] + kRescaleSlack) {
+        if (st.m_ref[j] != -INFINITY) st.l_part[j] *= __builtin_amdgcn_exp2f(st.m_ref[j] - mx);
+        st.m_ref[j] = mx;
+      }
+      const float m_use = (st.m_ref[j] == -INFINITY) ? 0.f : st.m_ref[j];
+      __bf16 pv[4];
+      float ls = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float e = __builtin_amdgcn_exp2f(sc[r] - m_use);
+        ls += e;
+        pv[r] = static_cast<__bf16>(e);
+      }
+      st.l_part[j] += ls;
+      *reinterpret_cast<uint2*>(pbuf + (t * 64 + lane) * 16 + st.th * 8) = __builtin_bit_cast(uint2, pv);
+      if (grp == 0) g_sm[i & 1][t][st.th][col] = st.m_ref[j];
     }
   }
 
-  template <int BUF>
-  __device__ __forceinline__ void clear_tail(int valid) {
-    char* tile = tile_buf<BUF>();
-    for (int i = valid * kChunks + threadIdx.x; i < kBlock * kChunks; i += W * 64)
-      *reinterpret_cast<uint4*>(tile + 16 * i) = uint4{0u, 0u, 0u, 0u};
+  // One iteration of the score waves; false once past the last one.
+  template <int U>
+  __device__ __forceinline__ bool score_iter(Score& st, int i, float qk_scale) {
+    if (i > n_sub) return false;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's P and references are written
+    lds_barrier();
+    if (i < n_sub) score_step<U>(st, i, qk_scale);
+    return true;
+  }
+
+  __device__ void run_score() {
+    Score st;
+    st.sg = wave >> 1;
+    st.th = wave & 1;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int row = (part * NT + 2 * st.sg + j) * 16 + col;
+      const int qi = row / p.H, qh = row % p.H;
+      st.n_vis[j] = L - p.s_q + 1 + qi;
+      const bf16_t* q = static_cast<const bf16_t*>(p.q) +
+                        (static_cast<int64_t>(b * p.s_q + qi) * p.H + qh) * kDQ + 8 * grp;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) st.qf[j][ks] = *reinterpret_cast<const bf16x8*>(q + 32 * ks);
+      st.m_ref[j] = -INFINITY;
+      st.l_part[j] = 0.f;
+    }
+    {
+      const int sw = swz(col);
+      const int lo2 = (grp ^ sw) & 3;
+      st.s_base_even = col * kRowBytes + 16 * ((0 ^ (sw & 4)) | lo2);
+      st.s_base_odd = col * kRowBytes + 16 * ((4 ^ (sw & 4)) | lo2);
+    }
+    const float qk_scale = p.scale * kLog2e;
+    stage_ids();
+    if (nb > 0) {
+      for (int i = 0;; i += 4) {
+        if (!score_iter<0>(st, i, qk_scale) || !score_iter<1>(st, i + 1, qk_scale) ||
+            !score_iter<2>(st, i + 2, qk_scale) || !score_iter<3>(st, i + 3, qk_scale))
+          break;
+      }
+    }
+    // Row sums (over the four lane groups) and final references for the value waves.
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float l = xor_sum(st.l_part[j]);
+      if (grp == 0) {
+        g_sl[2 * st.sg + j][st.th][col] = l;
+        g_sr[2 * st.sg + j][st.th][col] = st.m_ref[j];
+      }
+    }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     lds_barrier();
   }
 
-  // Scores S^T = C Q^T of tokens 32*th .. +32 for both score tiles; copy j of the next
-  // tile is issued after operand read 2j + 1.
-  template <int BUF>
-  __device__ __forceinline__ void score(f32x4 (&s)[2][2], const char* nxt) {
-    const char* tile = tile_buf<BUF>() + th * 32 * kRowBytes;
-    auto ld = [&](int i) {
-      const int ks = i >> 1, tt = i & 1;
-      return *reinterpret_cast<const bf16x8*>(tile + tt * 16 * kRowBytes + ((ks & 1) ? s_base_odd : s_base_even) +
-                                              128 * (ks >> 1));
-    };
+  // ---- value waves ----
+  struct Value {
+    int v;
+    f32x4 acc[NT][FQ];
+    float mv[NT];          // reference of acc for row `col` of each tile (log2 domain)
+    uint32_t coff[CPW];    // per-lane source offsets of this wave's copies within a sub-tile
+    int v_base[4];
+  };
+
+  // Copies of sub-tile k (block k / 2, half k % 2) into slot S.
+  template <int S>
+  __device__ __forceinline__ void issue_sub(const Value& vt, const char* block) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) s[j][0] = s[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bf16x8 a[NS];
-#pragma unroll
-    for (int i = 0; i < SB; ++i) a[i] = ld(i);
-#pragma unroll
-    for (int i = 0; i < NS; ++i) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        s[j][i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], qf[j][i >> 1], s[j][i & 1], 0, 0, 0);
-      if (i % SB == 0 && i + SB < NS) {
-#pragma unroll
-        for (int jj = 0; jj < SB; ++jj) a[i + SB + jj] = ld(i + SB + jj);
-      }
-      constexpr int GAP = NS / PER_WAVE;
-      if (i % GAP == GAP - 1) copy_at<1 - BUF>(i / GAP, nxt);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    for (int J = 0; J < CPW; ++J)
+      copy16_to_lds(block + vt.coff[J], (lds_void*)(sub_buf<S>() + (vt.v * CPW + J) * 1024));
   }
-  template <int BUF, int J = 0>
-  __device__ __forceinline__ void copy_at(int j, const char* src) {
-    if constexpr (J < PER_WAVE) {
-      if (j == J) issue_one<BUF, J>(src);
-      else copy_at<BUF, J + 1>(j, src);
-    }
+  __device__ __forceinline__ const char* sub_src(int k) const {
+    const int32_t id = __builtin_amdgcn_readfirstlane(max(g_ids[k >> 1], 0));
+    return static_cast<const char*>(p.kv) + static_cast<int64_t>(id) * kTileBytes + (k & 1) * kSubBytes;
   }
 
-  // O^T += C^T P^T over token half hh for this wave's 128 features and all four tiles.
-  template <int BUF>
-  __device__ __forceinline__ void value(int hh, const bf16x8 (&pb)[NT]) {
-    const char* tile = tile_buf<BUF>() + hh * 32 * kRowBytes + wave * 256;   // 128 B per 4 feature tiles
+  template <int SV>
+  __device__ __forceinline__ void value_step(Value& vt, int k) {
+    // The references and P^T of sub-tile k, then all transposed latent reads, in flight
+    // while the references are agreed.
+    float mh[2][NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) mh[h][t] = g_sm[k & 1][t][h][col];
+    bf16x8 pb[NT];
+    const char* pbuf = g_sp[k & 1];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) pb[t] = *reinterpret_cast<const bf16x8*>(pbuf + (t * 64 + lane) * 16);
+    const char* tile = sub_buf<SV>() + vt.v * 256;   // features 128 v .. +128
     auto tr = [&](int ft, int second) {
       return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(tile + v_base[ft & 3] + 128 * (ft >> 2) + second * 16 * kRowBytes));
+          (lds_i16x4*)(tile + vt.v_base[ft & 3] + 128 * (ft >> 2) + second * 16 * kRowBytes));
     };
     i16x4 lo[FQ], hi[FQ];
 #pragma unroll
     for (int ft = 0; ft < VB; ++ft) { lo[ft] = tr(ft, 0); hi[ft] = tr(ft, 1); }
+    bool mixed = false;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float M = fmaxf(mh[0][t], mh[1][t]);
+      const bool grow = M > vt.mv[t];
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // rare after the first sub-tiles
+        const float alpha = grow ? __builtin_amdgcn_exp2f(vt.mv[t] - M) : 1.f;   // 0 from -inf: acc is 0 then
+#pragma unroll
+        for (int ft = 0; ft < FQ; ++ft) vt.acc[t][ft] *= alpha;
+        if (grow) vt.mv[t] = M;
+      }
+      mixed |= mh[0][t] != vt.mv[t] || mh[1][t] != vt.mv[t];
+    }
+    if (__builtin_amdgcn_ballot_w64(mixed) != 0) {   // a half formed against a smaller reference
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float f = mh[h][t] < vt.mv[t] ? __builtin_amdgcn_exp2f(mh[h][t] - vt.mv[t]) : 1.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            pb[t][4 * h + e] = static_cast<__bf16>(static_cast<float>(pb[t][4 * h + e]) * f);
+        }
+      }
+    }
 #pragma unroll
     for (int ft = 0; ft < FQ; ++ft) {
       const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo[ft], hi[ft], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-        acc[t][ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[t], acc[t][ft], 0, 0, 0);
+      for (int t = 0; t < NT; ++t) vt.acc[t][ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[t], vt.acc[t][ft], 0, 0, 0);
       if (ft % VB == 0 && ft + VB < FQ) {
 #pragma unroll
         for (int jj = 0; jj < VB; ++jj) { lo[ft + VB + jj] = tr(ft + VB + jj, 0); hi[ft + VB + jj] = tr(ft + VB + jj, 1); }
@@ -658,111 +791,103 @@ struct AbsorbQuadCta {
     }
   }
 
-  __device__ __forceinline__ char* xp(int t, int h) { return g_qx + (t * 2 + h) * 1024; }
-  __device__ __forceinline__ float* xm(int t, int h) { return reinterpret_cast<float*>(g_qx + kQuadP) + (t * 2 + h) * 16; }
-
-  template <int BUF>
-  __device__ __forceinline__ void step(int k) {
-    __builtin_amdgcn_s_waitcnt(0);   // this block's copies have landed, this wave's LDS reads are done
+  // Iteration i of the value waves (slot U = i % 4 holds sub-tile i, (U + 3) % 4 sub-tile
+  // i - 1, (U + 2) % 4 receives sub-tile i + 2); false once past the last one.
+  template <int U>
+  __device__ __forceinline__ bool value_iter(Value& vt, int i) {
+    if (i > n_sub) return false;
+    wait_vmcnt<CPW>();                                   // sub-tile i has landed
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's zeroing is written
     lds_barrier();
-    if (k >= nb) return;
-    const int blk = blk_lo + k;
-    // The copies of the next tile always run; after the last block they repeat it into the
-    // idle buffer, which keeps the copy schedule free of branches.
-    const char* nxt = tile_src(min(k + 1, nb - 1));
-    if ((blk + 1) * kBlock > L) clear_tail<BUF>(L - blk * kBlock);
-    f32x4 s[2][2];
-    score<BUF>(s, nxt);
-    const int tb = blk * kBlock + th * 32 + 4 * grp;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int t = 2 * sg + j;
-      // m_ref of tile t, picked with a select chain: indexing the register array by the
-      // run-time row group would move it to scratch memory.
-      float mr = m_ref[0];
-#pragma unroll
-      for (int u = 1; u < NT; ++u) mr = (t == u) ? m_ref[u] : mr;
-      float sc[8];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float v = (tb + 16 * tt + r < n_vis[j]) ? s[j][tt][r] * qk_scale : -INFINITY;
-          sc[4 * tt + r] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = xor_max(mx);
-      float m_loc = mr;
-      if (mx > mr + kRescaleSlack) {
-        if (mr != -INFINITY) l_part[j] *= __builtin_amdgcn_exp2f(mr - mx);
-        m_loc = mx;
+    // The copies always run: past the last sub-tile they repeat it into the free slot,
+    // which keeps the count of copies in flight exact.
+    issue_sub<(U + 2) % 4>(vt, sub_src(min(i + 2, n_sub - 1)));
+    if (i < n_sub) {   // rows of sub-tile i past the context: zero, so the value product needs no mask
+      const int tok0 = (blk_lo * 2 + i) * kSubTok;
+      if (tok0 + kSubTok > L) {
+        char* tile = sub_buf<U>();
+        const int valid = max(0, L - tok0);
+        for (int e = valid * kChunks + (threadIdx.x - 256); e < kSubTok * kChunks; e += 256)
+          *reinterpret_cast<uint4*>(tile + 16 * e) = uint4{0u, 0u, 0u, 0u};
       }
-      const float m_use = (m_loc == -INFINITY) ? 0.f : m_loc;
-      bf16x8 pf;
-      float ls = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float v = __builtin_amdgcn_exp2f(sc[e] - m_use);
-        ls += v;
-        pf[e] = static_cast<__bf16>(v);
-      }
-      l_part[j] += ls;
-      *reinterpret_cast<bf16x8*>(xp(t, th) + 16 * lane) = pf;
-      if (grp == 0) xm(t, th)[col] = m_loc;
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    lds_barrier();
-    // Agreed references; rescale whatever was computed against a smaller one.
-    float ml[2][NT];
+    if (i >= 1) value_step<(U + 3) % 4>(vt, i - 1);
+    return true;
+  }
+
+  __device__ void run_value() {
+    Value vt;
+    vt.v = wave - 4;
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) ml[h][t] = xm(t, h)[col];
-    bool mixed = false;
+    for (int J = 0; J < CPW; ++J) vt.coff[J] = slot_source((vt.v * CPW + J) * 64 + lane);
+    // The first two sub-tiles (block 0 of the split) are copied before the block ids are
+    // staged; an id outside the pool is replaced by block 0 (it poisons the output anyway).
+    if (nb > 0) {
+      const int32_t id0 = p.block_table[static_cast<int64_t>(b) * p.max_blocks + blk_lo];
+      const char* blk0 = static_cast<const char*>(p.kv) +
+                         static_cast<int64_t>((id0 < 0 || id0 >= p.num_blocks) ? 0 : id0) * kTileBytes;
+      issue_sub<0>(vt, blk0);
+      issue_sub<1>(vt, blk0 + kSubBytes);
+    }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const float M = fmaxf(ml[0][t], ml[1][t]);
-      mixed |= ml[0][t] != ml[1][t];
-      const bool grow = M > m_ref[t];
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {   // rare after the first block
-        const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref[t] - M) : 1.f;   // 0 from -inf: acc is 0 then
+      vt.mv[t] = -INFINITY;
 #pragma unroll
-        for (int ft = 0; ft < FQ; ++ft) acc[t][ft] *= alpha;
-        if (t / 2 == sg) {
-          const float mine = ml[th][t];
-          if (mine < M && mine != -INFINITY) l_part[t & 1] *= __builtin_amdgcn_exp2f(mine - M);
-        }
-        if (grow) m_ref[t] = M;
+      for (int ft = 0; ft < FQ; ++ft) vt.acc[t][ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    {
+      const int src = 4 * grp + (col >> 2);
+      const int sw2 = swz(src);
+      const int m4 = col & 3;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        vt.v_base[q4] = src * kRowBytes + 16 * ((2 * q4 + (m4 >> 1)) ^ sw2) + 8 * (m4 & 1);
+    }
+    stage_ids();
+    if (nb > 0) {
+      for (int i = 0;; i += 4) {
+        if (!value_iter<0>(vt, i) || !value_iter<1>(vt, i + 1) || !value_iter<2>(vt, i + 2) ||
+            !value_iter<3>(vt, i + 3))
+          break;
       }
     }
-    const bool any_mixed = __builtin_amdgcn_ballot_w64(mixed) != 0;
+    __builtin_amdgcn_s_waitcnt(0);   // the repeated copies have landed before the workgroup ends
+    lds_barrier();                   // the score waves' row sums and references are written
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      bf16x8 pb[NT];
+    for (int t = 0; t < NT; ++t) {
+      const float l0 = g_sl[t][0][col], l1 = g_sl[t][1][col];
+      const float r0 = g_sr[t][0][col], r1 = g_sr[t][1][col];
+      const float M = vt.mv[t];
+      const float M_use = (M == -INFINITY) ? 0.f : M;
+      const float l = l0 * __builtin_amdgcn_exp2f(r0 - M_use) + l1 * __builtin_amdgcn_exp2f(r1 - M_use);
+      const int row = (part * NT + t) * 16 + col;
+      const int qi = row / p.H, qh = row % p.H;
+      const int64_t orow = static_cast<int64_t>(b * p.s_q + qi) * p.H + qh;
+      const bool empty = !(l > 0.f);
+      const float inv = empty ? 0.f : 1.f / l;
+      float* dst = (p.n_split == 1 ? static_cast<float*>(p.out) + orow * kDC
+                                   : p.ws_o + (orow * p.n_split + split) * kDC) + vt.v * 128 + 4 * grp;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) pb[t] = *reinterpret_cast<const bf16x8*>(xp(t, h) + 16 * lane);
-      if (any_mixed) {   // P of a half formed against a smaller reference than the agreed one
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const float mh = ml[h][t];
-          const float f = mh < m_ref[t] ? __builtin_amdgcn_exp2f(mh - m_ref[t]) : 1.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pb[t][e] = static_cast<__bf16>(static_cast<float>(pb[t][e]) * f);
+      for (int ft = 0; ft < FQ; ++ft) {
+        f32x4 o = vt.acc[t][ft] * inv;
+        if (bad) o = f32x4{nan_f32(), nan_f32(), nan_f32(), nan_f32()};
+        *reinterpret_cast<f32x4*>(dst + 16 * ft) = o;
+      }
+      if (vt.v == 0 && grp == 0) {
+        const float lse = bad ? nan_f32() : (empty ? -INFINITY : (M + __log2f(l)) * kLn2);
+        if (p.n_split == 1) {
+          if (p.lse != nullptr) p.lse[orow] = lse;
+        } else {
+          p.ws_lse[orow * p.n_split + split] = lse;
         }
       }
-      value<BUF>(h, pb);
     }
-    // No closing barrier: the next step's opening barrier is passed only once every wave
-    // has finished this one; the exchange area is rewritten only after it.
   }
 
   __device__ __forceinline__ void run(int unit, int part_) {
     part = part_;
     lane = threadIdx.x & 63;
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    sg = wave >> 1;
-    th = wave & 1;
     col = lane & 15;
     grp = lane >> 4;
     split = unit % p.n_split;
@@ -773,119 +898,26 @@ struct AbsorbQuadCta {
     blk_lo = split * p.blocks_per_split;
     const int blk_hi = bad ? blk_lo : min(nblk, blk_lo + p.blocks_per_split);
     nb = max(0, blk_hi - blk_lo);
-    // The first tile's copy starts before the rest of the prologue; the block ids (staged
-    // in LDS, -1 marking an id outside the pool) and the queries load while it runs.
-    const int32_t* table = p.block_table + static_cast<int64_t>(b) * p.max_blocks + blk_lo;
-    if (nb > 0) {
-      const int32_t id0 = table[0];
-      const int32_t c0 = (id0 < 0 || id0 >= p.num_blocks) ? 0 : id0;   // a bad id poisons the output anyway
-      issue_all<0>(static_cast<const char*>(p.kv) + static_cast<int64_t>(c0) * kTileBytes + wave * PER_WAVE * 1024);
-    }
-    constexpr int kIdsPerThread = kMaxSplitBlocks / (W * 64);
-    int32_t idr[kIdsPerThread];
-#pragma unroll
-    for (int u = 0; u < kIdsPerThread; ++u) {
-      const int i = threadIdx.x + u * W * 64;
-      idr[u] = i < nb ? table[i] : 0;
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int row = (part * NT + 2 * sg + j) * 16 + col;
-      const int qi = row / p.H, qh = row % p.H;
-      n_vis[j] = L - p.s_q + 1 + qi;
-      const bf16_t* q = static_cast<const bf16_t*>(p.q) +
-                        (static_cast<int64_t>(b * p.s_q + qi) * p.H + qh) * kDQ + 8 * grp;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qf[j][ks] = *reinterpret_cast<const bf16x8*>(q + 32 * ks);
-      l_part[j] = 0.f;
-    }
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      m_ref[t] = -INFINITY;
-#pragma unroll
-      for (int ft = 0; ft < FQ; ++ft) acc[t][ft] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    qk_scale = p.scale * kLog2e;
-    {
-      const int sw = swz(col);
-      const int lo2 = (grp ^ sw) & 3;
-      s_base_even = col * kRowBytes + 16 * ((0 ^ (sw & 4)) | lo2);
-      s_base_odd = col * kRowBytes + 16 * ((4 ^ (sw & 4)) | lo2);
-      const int src = 4 * grp + (col >> 2);
-      const int sw2 = swz(src);
-      const int m4 = col & 3;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        v_base[q4] = src * kRowBytes + 16 * ((2 * q4 + (m4 >> 1)) ^ sw2) + 8 * (m4 & 1);
-    }
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");   // ids, queries and the first tile
-#pragma unroll
-    for (int u = 0; u < kIdsPerThread; ++u) {
-      const int i = threadIdx.x + u * W * 64;
-      if (i < nb) g_ids[i] = (idr[u] < 0 || idr[u] >= p.num_blocks) ? -1 : idr[u];
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    lds_barrier();
-    for (int i = 0; i < nb; ++i) bad |= g_ids[i] < 0;
-    nb = bad ? 0 : nb;
-    for (int k = 0; k < nb; k += 2) {
-      step<0>(k);
-      step<1>(k + 1);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    lds_barrier();   // every copy has landed and every wave is done with the exchange area
-
-    // Row sums: each score wave's share, summed over lane groups and the two token halves.
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const float l = xor_sum(l_part[j]);
-      if (grp == 0) xm(2 * sg + j, th)[col] = l;
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    lds_barrier();
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const float l = xm(t, 0)[col] + xm(t, 1)[col];
-      const int row = (part * NT + t) * 16 + col;
-      const int qi = row / p.H, qh = row % p.H;
-      const int64_t orow = static_cast<int64_t>(b * p.s_q + qi) * p.H + qh;
-      const bool empty = !(l > 0.f);
-      const float inv = empty ? 0.f : 1.f / l;
-      float* dst = (p.n_split == 1 ? static_cast<float*>(p.out) + orow * kDC
-                                   : p.ws_o + (orow * p.n_split + split) * kDC) + wave * 128 + 4 * grp;
-#pragma unroll
-      for (int ft = 0; ft < FQ; ++ft) {
-        f32x4 v = acc[t][ft] * inv;
-        if (bad) v = f32x4{nan_f32(), nan_f32(), nan_f32(), nan_f32()};
-        *reinterpret_cast<f32x4*>(dst + 16 * ft) = v;
-      }
-      if (wave == 0 && grp == 0) {
-        const float lse = bad ? nan_f32() : (empty ? -INFINITY : (m_ref[t] + __log2f(l)) * kLn2);
-        if (p.n_split == 1) {
-          if (p.lse != nullptr) p.lse[orow] = lse;
-        } else {
-          p.ws_lse[orow * p.n_split + split] = lse;
-        }
-      }
-    }
+    if (wave < 4) run_score();
+    else run_value();
   }
 };
 
-__global__ __launch_bounds__(256, 1) void absorb_decode_quad(AttnParams p, int parts, int units) {
+__global__ __launch_bounds__(512, 1) void absorb_decode_spec(AttnParams p, int parts, int units) {
   const int x = blockIdx.x & 7, y = blockIdx.x >> 3;
   const int unit = parts == 1 ? static_cast<int>(blockIdx.x) : (y / parts) * 8 + x;
   const int part = parts == 1 ? 0 : y % parts;
   if (unit >= units) return;
-  AbsorbQuadCta cta(p);
+  AbsorbSpecCta cta(p);
   cta.run(unit, part);
 }
 
-hipError_t launch_quad(const AttnParams& p, int parts, hipStream_t s) {
+hipError_t launch_spec(const AttnParams& p, int parts, hipStream_t s) {
   if (p.blocks_per_split > kMaxSplitBlocks) return hipErrorInvalidValue;
   const int64_t units = static_cast<int64_t>(p.B) * p.n_split;
   const int64_t grid = parts == 1 ? units : ((units * parts + 8 * parts - 1) / (8 * parts)) * (8 * parts);
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  absorb_decode_quad<<<static_cast<unsigned>(grid), 256, 0, s>>>(p, parts, static_cast<int>(units));
+  absorb_decode_spec<<<static_cast<unsigned>(grid), 512, 0, s>>>(p, parts, static_cast<int>(units));
   return hipGetLastError();
 }
 
@@ -902,7 +934,7 @@ bool tuned_absorb_supported(const gqla_dims* d) {
          (rows == 16 || rows == 32 || rows == 64 || rows == 128 || rows == 256 || rows == 512);
 }
 
-// One 156 KiB workgroup per CU; each (sequence, split) unit takes absorb_parts() of them.
+// One workgroup per CU (148-158 KiB of LDS); each (sequence, split) unit takes absorb_parts() of them.
 int tuned_absorb_target_wgs(const gqla_dims* d) { return kNumCUs / absorb_parts(d); }
 
 int tuned_absorb_min_blocks_per_split() { return 4; }
@@ -913,13 +945,13 @@ hipError_t launch_tuned_absorb(const AttnParams& p, const gqla_dims* d, hipStrea
   switch (d->num_heads * d->s_q) {
     // Up to 32 rows each wave keeps its rows to itself: no P exchange, one barrier per
     // tile less (an exchanging layout measured 74 against 71 us on LLaMA-3-8B batch 32).
-    // From 64 rows the quad layout's shared operand reads win.
+    // From 64 rows the products go to separate waves (AbsorbSpecCta).
     case 16: return launch<1, 1, 2>(p, 1, s);
     case 32: return launch<1, 2, 2>(p, 1, s);
-    case 64: return launch_quad(p, 1, s);
-    case 128: return launch_quad(p, 2, s);
-    case 256: return launch_quad(p, 4, s);
-    case 512: return launch_quad(p, 8, s);
+    case 64: return launch_spec(p, 1, s);
+    case 128: return launch_spec(p, 2, s);
+    case 256: return launch_spec(p, 4, s);
+    case 512: return launch_spec(p, 8, s);
   }
   return hipErrorNotSupported;
 }

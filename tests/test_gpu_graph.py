@@ -1,5 +1,6 @@
 """The decode calls under HIP graph capture: one step (append of the new tokens, absorb
-path with its split combine, GQA path) captured once and replayed several times, with
+path with its split combine, the same decode through gqla_decode_absorb_out with the combine
+fused into the value projection, GQA path) captured once and replayed several times, with
 eager work and synchronisations between the replays, gives the eager step's outputs bit
 for bit each time (the library records no memset nodes; its kernels are deterministic)."""
 import numpy as np
@@ -42,13 +43,15 @@ def test_captured_step_replays_match_eager(name):
     ws_abs, ws_gqa = ws(d_abs, G.GQLA_PATH_ABSORB), ws(d_gqa, G.GQLA_PATH_GQA)
     assert G.gqla_num_splits(d_abs, G.GQLA_PATH_ABSORB, run.table.shape[1], run.paged.max_ctx_len,
                              x.num_blocks, 3) > 1   # the combine is part of the captured step
-    outs = (out_abs, out_gqa, lse_gqa, o_lat)
+    o_lat2, out_abs2 = torch.empty_like(o_lat), torch.empty_like(out_abs)
+    outs = (out_abs, out_gqa, lse_gqa, o_lat, o_lat2, out_abs2)
 
     def step():
         G.gqla_append_tokens(d_gqa, run.paged, c_app, kr_app, 10000.0, run.w_uk, run.w_uv, run.cache, expanded)
         G.gqla_absorb_query(d_abs, q_nope1, q_rope1, run.w_uk, q_abs)
         G.gqla_decode_absorb(d_abs, paged_abs, q_abs, run.cache, ws_abs, o_lat)
         G.gqla_out_proj(d_abs, o_lat, run.w_uv, out_abs)
+        G.gqla_decode_absorb_out(d_abs, paged_abs, q_abs, run.cache, run.w_uv, ws_abs, o_lat2, out_abs2)
         G.gqla_decode_gqa(d_gqa, run.paged, run.q, expanded, ws_gqa, out_gqa, lse_gqa)
 
     log(f"graph capture {name}")
@@ -56,6 +59,9 @@ def test_captured_step_replays_match_eager(name):
     torch.cuda.synchronize()
     ref = [t.clone() for t in outs]
     assert all(torch.isfinite(t).all() for t in ref)
+    # the two absorb forms differ only in the order of the combine's sums
+    assert float((o_lat2 - o_lat).abs().max()) <= 1e-5 * float(o_lat.abs().max())
+    assert float((out_abs2.float() - out_abs.float()).abs().max()) <= 1e-2 * float(out_abs.float().abs().max())
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
