@@ -26,7 +26,7 @@ namespace gqla {
 // (~15 us for the absorb decode by per-workgroup timestamps on LLaMA-3-8B batch 32).
 struct Mi355xRates {
   double absorb_bw = 6.2e12;      // absorb decode latent streaming, B/s (tile copies into LDS)
-  double absorb_mfma = 0.8e15;    // absorb decode when MFMA/LDS-bound, flop/s
+  double absorb_mfma = 0.9e15;    // absorb decode when MFMA/LDS-bound, flop/s (specialized waves)
   double absorb_fixed_us = 15.0;  // absorb decode fixed cost
   double gqa_bw = 6.8e12;         // GQA decode expanded-cache streaming, B/s (per-group layout)
   double gqa_shared_bw = 7.0e12;  // same, RoPE key once per block
