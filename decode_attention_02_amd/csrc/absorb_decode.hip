@@ -720,12 +720,15 @@ struct AbsorbSpecCta {
     int v_base[4];
   };
 
-  // Copies of sub-tile k (block k / 2, half k % 2) into slot S.
+  // Copies of sub-tile k (block k / 2, half k % 2) into slot S. Cache-retaining loads: the
+  // other row parts of the sequence (on the same XCD) read the same sub-tile from L2; with
+  // non-temporal loads they missed there and HBM reads were 1.35-1.47x the latent bytes at
+  // 128 and 256 rows, with these 1.03x.
   template <int S>
   __device__ __forceinline__ void issue_sub(const Value& vt, const char* block) {
 #pragma unroll
     for (int J = 0; J < CPW; ++J)
-      copy16_to_lds(block + vt.coff[J], (lds_void*)(sub_buf<S>() + (vt.v * CPW + J) * 1024));
+      __builtin_amdgcn_global_load_lds(block + vt.coff[J], (lds_void*)(sub_buf<S>() + (vt.v * CPW + J) * 1024), 16, 0, 0);
   }
   __device__ __forceinline__ const char* sub_src(int k) const {
     const int32_t id = __builtin_amdgcn_readfirstlane(max(g_ids[k >> 1], 0));
