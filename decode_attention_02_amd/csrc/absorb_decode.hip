@@ -57,9 +57,6 @@ constexpr float kLn2 = 0.6931471805599453f;
 // reads (8 rows, a chunk pair each), distinct swz >> 1 among same-parity rows of each
 // aligned 8: swz(t) = (t mod 8) xor bit 3 of t satisfies both and has period 16.
 __device__ __forceinline__ int swz(int t) { return (t & 7) ^ ((t >> 3) & 1); }
-__device__ __forceinline__ int chunk_off(int t, int c) {
-  return t * kRowBytes + (((c & ~7) | ((c & 7) ^ swz(t))) << 4);
-}
 
 // Reductions over the four 16-lane rows of a wave (lanes l, l ^ 16, l ^ 32, l ^ 48) with
 // gfx950's row-swap instructions: v_permlane16_swap exchanges rows 0 <-> 1 and 2 <-> 3

@@ -147,13 +147,16 @@ hipError_t launch_generic_attn(const AttnParams& p, bool bf16, hipStream_t s) {
   const int rows_total = p.heads_per_kv * p.s_q;
   dim3 grid(p.n_split, (rows_total + kGenRows - 1) / kGenRows, p.B * p.kv_heads);
   const size_t lds = generic_attn_lds_bytes(p.dk, p.dvo);
+  hipError_t e;
   if (bf16) {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(&generic_attn_split<bf16_t>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&generic_attn_split<bf16_t>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
     generic_attn_split<bf16_t><<<grid, kGenThreads, lds, s>>>(p);
   } else {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(&generic_attn_split<float>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&generic_attn_split<float>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
     generic_attn_split<float><<<grid, kGenThreads, lds, s>>>(p);
   }
   return hipGetLastError();

@@ -219,6 +219,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 template <int S>
 __device__ __forceinline__ char* stage_buf() {
+  static_assert(S >= 0 && S < kDmaStages, "stage");
   return S == 0 ? g_st0 : S == 1 ? g_st1 : S == 2 ? g_st2 : g_st3;
 }
 
@@ -356,7 +357,7 @@ __global__ __launch_bounds__(256) void generic_hidden(const TX* x, const T* w, T
 // W_fold[n][h*d_c + c] = sum_v W_O[n][h*d_v + v] W_UV^g[v][c]; one thread per element,
 // threads along c (coalesced W_UV reads, W_O broadcast).
 template <typename T>
-__global__ __launch_bounds__(256) void fold_kernel(ProjParams d, int hidden, const T* w_o, const T* w_uv, T* w_fold) {
+__global__ __launch_bounds__(256) void fold_kernel(ProjParams d, const T* w_o, const T* w_uv, T* w_fold) {
   const int c = blockIdx.x * blockDim.x + threadIdx.x;
   const int h = blockIdx.y;
   const int n = blockIdx.z;
@@ -401,10 +402,10 @@ hipError_t launch_fold_out_weight(const ProjParams& p, int hidden, const void* w
                                   bool bf16, hipStream_t s) {
   const dim3 grid((p.dc + 255) / 256, p.H, hidden);
   if (bf16)
-    fold_kernel<bf16_t><<<grid, 256, 0, s>>>(p, hidden, static_cast<const bf16_t*>(w_o), static_cast<const bf16_t*>(w_uv),
+    fold_kernel<bf16_t><<<grid, 256, 0, s>>>(p, static_cast<const bf16_t*>(w_o), static_cast<const bf16_t*>(w_uv),
                                              static_cast<bf16_t*>(w_fold));
   else
-    fold_kernel<float><<<grid, 256, 0, s>>>(p, hidden, static_cast<const float*>(w_o), static_cast<const float*>(w_uv),
+    fold_kernel<float><<<grid, 256, 0, s>>>(p, static_cast<const float*>(w_o), static_cast<const float*>(w_uv),
                                             static_cast<float*>(w_fold));
   return hipGetLastError();
 }
