@@ -545,7 +545,7 @@ struct AbsorbSpecCta {
   static constexpr int FQ = kDC / 16 / 4;       // feature tiles per value wave (8)
   static constexpr int CPW = kSubCopies / 4;    // copies per value wave per sub-tile (9)
   static constexpr int SB = 9;                  // score operand reads per batch
-  static constexpr int VB = 8;                  // value feature tiles per batch (all of them)
+  static constexpr int VB = 4;                  // value feature tiles per batch
   static_assert(KS % SB == 0 && FQ % VB == 0, "batches");
   static_assert(CPW * 4 == kSubCopies, "sub-tile copies split over the value waves");
 
@@ -728,15 +728,16 @@ struct AbsorbSpecCta {
     for (int J = 0; J < CPW; ++J)
       __builtin_amdgcn_global_load_lds(block + vt.coff[J], (lds_void*)(sub_buf<S>() + (vt.v * CPW + J) * 1024), 16, 0, 0);
   }
-  __device__ __forceinline__ const char* sub_src(int k) const {
-    const int32_t id = __builtin_amdgcn_readfirstlane(max(g_ids[k >> 1], 0));
+  __device__ __forceinline__ const char* sub_src(int32_t id, int k) const {
+    id = __builtin_amdgcn_readfirstlane(max(id, 0));
     return static_cast<const char*>(p.kv) + static_cast<int64_t>(id) * kTileBytes + (k & 1) * kSubBytes;
   }
 
   template <int SV>
   __device__ __forceinline__ void value_step(Value& vt, int k) {
-    // The references and P^T of sub-tile k, then all transposed latent reads, in flight
-    // while the references are agreed.
+    // The references and P^T of sub-tile k, then the first batch of transposed latent
+    // reads, in flight while the references are agreed (the LDS counter can wait for the
+    // references with at most 15 later reads outstanding).
     float mh[2][NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
@@ -797,12 +798,15 @@ struct AbsorbSpecCta {
   template <int U>
   __device__ __forceinline__ bool value_iter(Value& vt, int i) {
     if (i > n_sub) return false;
+    // The copies always run: past the last sub-tile they repeat it into the free slot,
+    // which keeps the count of copies in flight exact. Their block id is read from LDS
+    // before the waits, which cover its latency.
+    const int k_next = min(i + 2, n_sub - 1);
+    const int32_t id_next = g_ids[k_next >> 1];
     wait_vmcnt<CPW>();                                   // sub-tile i has landed
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's zeroing is written
     lds_barrier();
-    // The copies always run: past the last sub-tile they repeat it into the free slot,
-    // which keeps the count of copies in flight exact.
-    issue_sub<(U + 2) % 4>(vt, sub_src(min(i + 2, n_sub - 1)));
+    issue_sub<(U + 2) % 4>(vt, sub_src(id_next, k_next));
     if (i < n_sub) {   // rows of sub-tile i past the context: zero, so the value product needs no mask
       const int tok0 = (blk_lo * 2 + i) * kSubTok;
       if (tok0 + kSubTok > L) {
