@@ -15,8 +15,9 @@
 // the rows' inputs, which every workgroup shares, from L2, each input operand feeding
 // one MFMA per weight tile. The 4 partial results are summed through LDS. An fp32 input
 // is split into bf16 high and low parts (two MFMAs), which keeps the product close to fp32
-// accuracy. Wide layers with bf16 inputs (hidden >= 8192) use a second form that stages
-// both operands through LDS (hidden_dma below).
+// accuracy. With bf16 inputs, most shapes use a form that streams the weight through LDS in
+// 512-byte runs per row (hidden_ks below); wide layers whose contraction is not whole
+// 256-element chunks stage both operands through LDS in 256-byte runs (hidden_dma).
 #include "device_common.h"
 #include "gqla_internal.h"
 
@@ -342,6 +343,199 @@ hipError_t launch_dma(const void* x, const void* w, void* y, int M, int N, int K
   return hipGetLastError();
 }
 
+// bf16 inputs and a contraction in whole 256-element chunks: the 16 RT weight rows of a
+// workgroup stream through an LDS ring in 512-byte runs per row (at the row stride of a wide
+// layer, 256-byte runs read HBM at ~4.4 TB/s on MI355X and 512-byte runs at ~5.9), NS - 1
+// chunks ahead; the inputs, which every workgroup reads (L2-resident), go straight into
+// registers two chunks ahead, so LDS holds weight only. Each wave takes a quarter of every
+// chunk's contraction for all the workgroup's weight rows and 16 MT input rows, and the four
+// partial results are summed through LDS at the end. RT = 1, 2, 4 (16, 32, 64 rows) keeps
+// about one round of workgroups on the CUs for any output width.
+constexpr int kKsChunk = 256;                         // contraction per chunk (512 bytes of a row)
+constexpr int kKsRingBytes = 128 * 1024;
+
+template <int MT, int RT>
+struct KsShape {
+  static constexpr int kRows = 16 * RT;
+  static constexpr int kStage = kRows * kKsChunk * 2;          // bytes per chunk
+  static constexpr int kStages = RT == 4 ? 4 : 8;               // ring (in flight: kStages - 1)
+  static constexpr int kLds = kStages * kStage;                 // 64 KiB for RT = 1: two per CU
+  static constexpr int kCPW = kStage / 1024 / kWaves;          // 1 KiB copies per wave per chunk
+  static constexpr int kXL = 2 * MT;                            // input loads per wave per chunk
+  static constexpr int kPerCU = RT == 1 ? 2 : 1;
+  static_assert(kLds <= kKsRingBytes && kCPW >= 1 && kStages % 4 == 0, "ring");
+  static_assert(2 * kCPW + kXL < 64, "vmcnt range");
+  static_assert(kWaves * RT * MT * 1024 <= kLds, "partials fit the ring");
+};
+
+template <int MT, int RT>
+__global__ __launch_bounds__(256, (KsShape<MT, RT>::kPerCU)) void hidden_ks(const bf16_t* x, const bf16_t* w, bf16_t* y,
+                                                                          int M, int N, int K) {
+  using Sh = KsShape<MT, RT>;
+  __shared__ __attribute__((aligned(16))) char g_ks[Sh::kLds];
+  constexpr int CPW = Sh::kCPW, NS = Sh::kStages, D = NS - 1;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int n0 = blockIdx.x * Sh::kRows;
+  const int m0 = blockIdx.y * 16 * MT;
+  const int nch = K / kKsChunk;
+  const char* wbase = reinterpret_cast<const char*>(w + static_cast<int64_t>(n0) * K);
+  // Copy slot s of a stage holds weight row s / 32, 16-byte piece (s % 32) ^ (row % 16) of
+  // the chunk's 512 bytes: the XOR spreads the 16 rows of an operand read over all banks.
+  uint32_t off[CPW];
+#pragma unroll
+  for (int j = 0; j < CPW; ++j) {
+    const int slot = (wave * CPW + j) * 64 + lane;
+    const int row = slot >> 5, piece = (slot & 31) ^ (row & 15);
+    off[j] = static_cast<uint32_t>(row) * static_cast<uint32_t>(K) * 2u + 16u * piece;
+  }
+  // Input operand of tile t, step ks: row m0 + 16 t + col (rows past M re-read row M - 1 and
+  // are never stored), elements 64 wave + 32 ks + 8 grp of the chunk.
+  uint32_t xoff[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+    xoff[t] = static_cast<uint32_t>(min(m0 + 16 * t + col, M - 1)) * static_cast<uint32_t>(K) + 64 * wave + 8 * grp;
+
+  auto stage = [](int S) { return g_ks + S * Sh::kStage; };
+  auto copies = [&](int c, char* st) {
+    const char* src = wbase + static_cast<int64_t>(min(c, nch - 1)) * (kKsChunk * 2);   // past the end: the last chunk again
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+      uint32_t o = off[j];
+      asm volatile("" : "+v"(o));   // a separate 32-bit operand, so the copy takes a scalar base
+      __builtin_amdgcn_global_load_lds(src + o, (lds_void*)(st + (wave * CPW + j) * 1024), 16, 0, 2);
+    }
+  };
+  bf16x8 xb[4][MT][2];
+  auto inputs = [&](int c, bf16x8 (&dst)[MT][2]) {
+    const bf16_t* xc = x + min(c, nch - 1) * kKsChunk;
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) dst[t][ks] = *reinterpret_cast<const bf16x8*>(xc + xoff[t] + 32 * ks);
+  };
+  f32x4 acc[RT][MT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const char* st, const bf16x8 (&xs)[MT][2]) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int pc = 16 * ((8 * wave + 4 * ks + grp) ^ col);
+      bf16x8 a[RT];
+#pragma unroll
+      for (int r = 0; r < RT; ++r) a[r] = *reinterpret_cast<const bf16x8*>(st + (16 * r + col) * (kKsChunk * 2) + pc);
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[r], xs[t][ks], acc[r][t], 0, 0, 0);
+    }
+  };
+  // Issue order: weight chunk c + D follows input chunk c + 2, so waiting for the inputs of
+  // chunk c leaves the copies of c + D - 2 and c + D - 1 and the inputs of c + 1 in flight
+  // (chunk c's copies went out before its inputs); the barrier then also frees stage
+  // (c + D) % NS, read in step c - 1.
+  auto step = [&](int c, auto si) {
+    constexpr int S = decltype(si)::value;
+    dma_wait_vmcnt<2 * CPW + Sh::kXL>();
+    dma_barrier();
+    inputs(c + 2, xb[(S + 2) & 3]);
+    copies(c + D, stage((S + D) % NS));
+    compute(stage(S), xb[S & 3]);
+  };
+#pragma unroll
+  for (int c = 0; c < D - 2; ++c) copies(c, stage(c));
+  inputs(0, xb[0]);
+  copies(D - 2, stage(D - 2));
+  inputs(1, xb[1]);
+  copies(D - 1, stage(D - 1));
+  const int nfull = nch - nch % NS;
+  int c = 0;
+  for (; c < nfull; c += NS) {
+    step(c, std::integral_constant<int, 0>());
+    step(c + 1, std::integral_constant<int, 1>());
+    step(c + 2, std::integral_constant<int, 2>());
+    step(c + 3, std::integral_constant<int, 3>());
+    if constexpr (NS == 8) {
+      step(c + 4, std::integral_constant<int, 4>());
+      step(c + 5, std::integral_constant<int, 5>());
+      step(c + 6, std::integral_constant<int, 6>());
+      step(c + 7, std::integral_constant<int, 7>());
+    }
+  }
+  // The remaining 0 .. NS - 1 chunks (an exit inside an unrolled round would make the
+  // compiler's wait analysis drain every load in flight).
+  if (c < nch) step(c, std::integral_constant<int, 0>());
+  if (c + 1 < nch) step(c + 1, std::integral_constant<int, 1>());
+  if (c + 2 < nch) step(c + 2, std::integral_constant<int, 2>());
+  if constexpr (NS == 8) {
+    if (c + 3 < nch) step(c + 3, std::integral_constant<int, 3>());
+    if (c + 4 < nch) step(c + 4, std::integral_constant<int, 4>());
+    if (c + 5 < nch) step(c + 5, std::integral_constant<int, 5>());
+    if (c + 6 < nch) step(c + 6, std::integral_constant<int, 6>());
+  }
+  dma_wait_vmcnt<0>();   // the loads past the end have landed before the ring is reused
+  dma_barrier();         // every wave's last product has read its stage
+  // Partials of wave q at [q][r][t][lane] (f32x4: features 16 r + 4 grp .. +4 of input row
+  // 16 t + col); then each thread sums some of them over the waves.
+  f32x4* red = reinterpret_cast<f32x4*>(g_ks);
+  constexpr int kPart = RT * MT * 64;
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) red[wave * kPart + (r * MT + t) * 64 + lane] = acc[r][t];
+  __syncthreads();
+  for (int e = threadIdx.x; e < kPart; e += 256) {
+    f32x4 v = red[e];
+#pragma unroll
+    for (int q = 1; q < kWaves; ++q) v += red[q * kPart + e];
+    const int ln = e & 63, t = (e >> 6) % MT, r = (e >> 6) / MT;
+    const int m = m0 + 16 * t + (ln & 15);
+    if (m < M) {
+      bf16_t packed[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) packed[i] = f32_to_bf16(v[i]);
+      *reinterpret_cast<uint2*>(y + static_cast<int64_t>(m) * N + n0 + 16 * r + 4 * (ln >> 4)) =
+          *reinterpret_cast<uint2*>(packed);
+    }
+  }
+}
+
+template <int MT, int RT>
+hipError_t launch_ks_rt(const void* x, const void* w, void* y, int M, int N, int K, hipStream_t s) {
+  const dim3 grid(N / (16 * RT), (M + 16 * MT - 1) / (16 * MT));
+  hidden_ks<MT, RT><<<grid, 256, 0, s>>>(static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(w),
+                                         static_cast<bf16_t*>(y), M, N, K);
+  return hipGetLastError();
+}
+
+// Weight rows per workgroup of the 512-byte-run form for a bf16 product, 0 where another
+// form is faster. Measured on MI355X (median after a 1 GiB read): 64 rows when that fills
+// the CUs (16384 x 16384 at 16-64 input rows: 89-111 us against 129-153 us for the
+// 256-byte-run form); 32 rows where the 256-byte-run form has under 128 workgroups
+// (7168 x 16384, 64 rows: 81 against 158 us for the per-wave form), not at 8192 x 4096
+// (26 against 22 us); 16 rows, two workgroups per CU, for 4096 x 4096 from 17 input rows
+// (16.0 against 17.1 us at 32 rows; 10.9 against 10.1 at one row).
+int ks_rows(int M, int N, int K) {
+  if (K % kKsChunk != 0 || K > (1 << 20)) return 0;
+  if (N % 64 == 0 && N / 64 >= kNumCUs) return 64;
+  if (N % 64 == 0 && N / 64 >= kNumCUs / 2) return 0;
+  if (N % 32 == 0 && N / 32 >= kNumCUs * 7 / 8) return 32;
+  if (M > 16 && N % 16 == 0 && N / 16 >= kNumCUs) return 16;
+  return 0;
+}
+
+template <int MT>
+hipError_t launch_ks(const void* x, const void* w, void* y, int M, int N, int K, hipStream_t s) {
+  switch (ks_rows(M, N, K)) {
+    case 64: return launch_ks_rt<MT, 4>(x, w, y, M, N, K, s);
+    case 32: return launch_ks_rt<MT, 2>(x, w, y, M, N, K, s);
+    default: return launch_ks_rt<MT, 1>(x, w, y, M, N, K, s);
+  }
+}
+
 // Generic: one thread per output, fp32 accumulation; any sizes, fp32 or bf16 data.
 template <typename T, typename TX>
 __global__ __launch_bounds__(256) void generic_hidden(const TX* x, const T* w, T* y, int M, int N, int K) {
@@ -375,6 +569,11 @@ __global__ __launch_bounds__(256) void fold_kernel(ProjParams d, const T* w_o, c
 hipError_t launch_out_hidden(const void* x, bool x_f32, const void* w, void* y, int M, int N, int K, bool bf16,
                              hipStream_t s) {
   if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
+  if (bf16 && !x_f32 && ks_rows(M, N, K) != 0) {
+    if (M <= 16) return launch_ks<1>(x, w, y, M, N, K, s);
+    if (M <= 32) return launch_ks<2>(x, w, y, M, N, K, s);
+    return launch_ks<4>(x, w, y, M, N, K, s);
+  }
   if (bf16 && !x_f32 && N % 64 == 0 && N / 64 >= kNumCUs / 2 && K % 128 == 0 && K <= (1 << 20)) {
     if (M <= 16) return launch_dma<1>(x, w, y, M, N, K, s);
     if (M <= 32) return launch_dma<2>(x, w, y, M, N, K, s);

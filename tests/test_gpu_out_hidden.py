@@ -2,8 +2,9 @@
 oracle, on seeded host inputs: W_O over the heads' outputs, the fold of W_UV^g into W_O, and
 the folded projection over the absorb path's fp32 latent outputs. Row counts cover one row,
 a ragged last 16-row tile and several row passes; hidden sizes cover the module's
-H * head_dim, untied sizes (both weight-streaming forms: per-wave register chunks, and 64-row
-LDS-staged chunks from hidden 8192 up) and one that is not a multiple of 16 (generic kernel)."""
+H * head_dim, untied sizes (every weight-streaming form: per-wave register chunks, and from
+hidden 8192 up 64-row LDS-staged chunks, 512 bytes of each row when the contraction is whole
+256-element chunks, else 256) and one that is not a multiple of 16 (generic kernel)."""
 import zlib
 
 import numpy as np
@@ -24,11 +25,18 @@ SHAPES = {
     "llama3-8b": (32, 8, 512, 128, "bf16"),
     "dsv3": (128, 16, 512, 128, "bf16"),
     "dsv3-tp8share": (16, 2, 512, 128, "bf16"),
-    # head counts whose contraction H * d_v is 1, 10 and 19 chunks of 128: the LDS-staged
-    # form's 4-chunk ring then ends in a tail of 1, 2 and 3 chunks
+    # head counts whose contraction H * d_v is 1 and 19 chunks of 128 (not whole 256-element
+    # chunks: the LDS-staged form with 128-element chunks, its 4-chunk ring ending in a tail
+    # of 1 and 3 chunks) ...
     "h1": (1, 1, 512, 128, "bf16"),
-    "h10": (10, 2, 512, 128, "bf16"),
     "h19": (19, 1, 512, 128, "bf16"),
+    # ... and 1, 3, 5, 7 and 11 chunks of 256 (the 512-byte-run form, with rings of 4 chunks
+    # at 64 rows per workgroup and of 8 at 16 and 32: no whole ring, or tails after one)
+    "h2": (2, 1, 512, 128, "bf16"),
+    "h6": (6, 2, 512, 128, "bf16"),
+    "h10": (10, 2, 512, 128, "bf16"),
+    "h14": (14, 2, 512, 128, "bf16"),
+    "h22": (22, 2, 512, 128, "bf16"),
 }
 
 
@@ -56,6 +64,8 @@ def _dims(H, Gr, dc, dv, dtype, B, s_q):
     # tiles, a ragged last tile, and two passes over the rows
     ("dsv3", 16384, 64, 1), ("dsv3", 8192, 70, 1), ("llama3-8b", 8192, 20, 1), ("llama3-8b", 16384, 13, 1),
     ("h1", 8192, 5, 1), ("h10", 8192, 33, 1), ("h19", 16384, 17, 1),
+    ("h2", 8192, 3, 1), ("h6", 8192, 40, 1), ("h14", 16384, 64, 1), ("h14", 8192, 80, 1),
+    ("h6", 7168, 40, 1), ("h10", 7200, 20, 1), ("h14", 4096, 33, 1), ("h2", 6144, 17, 1), ("h22", 4096, 24, 1),
     ("dsv3-tp8share", 2048, 9, 2),
 ])
 def test_out_hidden_matches_oracle(name, hidden, B, s_q):
