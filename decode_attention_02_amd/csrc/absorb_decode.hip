@@ -735,9 +735,9 @@ struct AbsorbSpecCta {
 
   template <int SV>
   __device__ __forceinline__ void value_step(Value& vt, int k) {
-    // The references and P^T of sub-tile k, then the first batch of transposed latent
-    // reads, in flight while the references are agreed (the LDS counter can wait for the
-    // references with at most 15 later reads outstanding).
+    // The references and P^T of sub-tile k, then the first half of the transposed latent
+    // reads, in flight while the references are agreed; the second half is issued under
+    // the first products.
     float mh[2][NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
