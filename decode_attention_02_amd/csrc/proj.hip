@@ -20,10 +20,16 @@
 //     split into bf16 high and low parts (two MFMAs) so the product keeps close to fp32
 //     accuracy.
 // Workgroups are small (one wave; four for the absorbed query at large row counts) so the
-// weight and row reads of a small batch spread over most CUs instead of a few.
+// weight and row reads of a small batch spread over most CUs instead of a few. At large
+// batches the value projection's fp32 latent outputs are the stream and get a form of their
+// own (out_proj_stream: one four-wave workgroup per CU and group, each o_lat tile read once
+// into an LDS ring and shared by the four waves).
 #include "device_common.h"
 #include "gqla_internal.h"
 #include "tuned.h"
+
+#include <algorithm>
+#include <type_traits>
 
 namespace gqla {
 namespace {
@@ -214,6 +220,122 @@ __global__ __launch_bounds__(64) void out_proj_kernel(ProjParams d, const float*
       }
     }
   }
+}
+
+// Value projection over many rows (large batches), where the latent outputs are the
+// stream: one workgroup per (group, run of 16-row tiles), its four waves holding W_UV^g rows
+// 32w .. +32 in registers and sharing each tile of o_lat, which goes through an LDS ring
+// (global_load_lds, three tiles ahead). Every latent output is then read from memory once,
+// instead of once per 32 output features by the single-wave form.
+constexpr int kOpTileBytes = 16 * kDC * 4;             // 16 rows of fp32 o_lat: 32 KiB
+constexpr int kOpStages = 4;
+constexpr int kOpCPW = kOpTileBytes / 1024 / 4;        // 1 KiB copies per wave per tile (8)
+
+template <int N>
+__device__ __forceinline__ void op_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+}
+
+__global__ __launch_bounds__(256, 1) void out_proj_stream(ProjParams d, const float* o_lat, const bf16_t* w_uv,
+                                                          bf16_t* out, int nx) {
+  __shared__ __attribute__((aligned(16))) char ring[kOpStages * kOpTileBytes];
+  const int g = blockIdx.x / nx, x = blockIdx.x % nx;
+  const int gs = d.H / d.G;
+  const int rows_g = d.rows * gs;
+  const int n_rt = (rows_g + 15) / 16;
+  if (x >= n_rt) return;
+  const int nt = (n_rt - x + nx - 1) / nx;   // tiles x, x + nx, ... of this workgroup
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  bf16x8 wa[2][kDC / 32];
+  {
+    const bf16_t* wsrc = w_uv + (static_cast<int64_t>(g) * kDV + 32 * wave + col) * kDC + 8 * grp;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int ks = 0; ks < kDC / 32; ++ks) wa[t][ks] = *reinterpret_cast<const bf16x8*>(wsrc + 16 * t * kDC + 32 * ks);
+  }
+  auto stage = [&](int S) __attribute__((always_inline)) { return ring + S * kOpTileBytes; };
+  // Copy j of a wave fills LDS chunks (8 wave + j) * 64 + lane of the tile: row (8 wave + j)
+  // / 2 (the same for the whole wave), position p = 64 ((8 wave + j) % 2) + lane of its 128
+  // 16-byte chunks, which holds source chunk p ^ row (rows 0..15), so the 16 rows of an
+  // operand read sit in 16 different bank groups.
+  auto copies = [&](int j, char* st) __attribute__((always_inline)) {
+    const int rt = x + min(j, nt - 1) * nx;   // past the end: the last tile again
+#pragma unroll
+    for (int k = 0; k < kOpCPW; ++k) {
+      const int c = wave * kOpCPW + k;
+      const int row = c >> 1;
+      const int rg = min(rt * 16 + row, rows_g - 1);
+      const float* src = o_lat + group_row(rg, g, gs, d.H) * kDC;
+      uint32_t off = 16u * static_cast<uint32_t>((64 * (c & 1) + lane) ^ row);
+      asm volatile("" : "+v"(off));   // a separate 32-bit operand, so the copy takes a scalar base
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(src) + off, (lds_void*)(st + c * 1024), 16, 0, 2);
+    }
+  };
+  auto compute = [&](int j, const char* st) __attribute__((always_inline)) {
+    const char* rowp = st + col * (kDC * 4);
+    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < kDC / 32; ++ks) {
+      const int c0 = 8 * ks + 2 * grp;
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(rowp + 16 * (c0 ^ col));
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(rowp + 16 * ((c0 + 1) ^ col));
+      bf16x8 hi, lo;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float v = k < 4 ? x0[k] : x1[k - 4];
+        const __bf16 h = static_cast<__bf16>(v);
+        hi[k] = h;
+        lo[k] = static_cast<__bf16>(v - static_cast<float>(h));
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[t][ks], hi, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[t][ks], lo, acc[t], 0, 0, 0);
+      }
+    }
+    const int rg = (x + j * nx) * 16 + col;
+    if (rg < rows_g) {
+      const int64_t orow = group_row(rg, g, gs, d.H);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        bf16_t packed[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) packed[k] = f32_to_bf16(acc[t][k]);
+        *reinterpret_cast<uint2*>(out + orow * kDV + 32 * wave + 16 * t + 4 * grp) = *reinterpret_cast<uint2*>(packed);
+      }
+    }
+  };
+  // Tile j in stage j % 4: wait for its copies (j + 1 and j + 2 may stay in flight; the
+  // weight loads went out first), pass the barrier that also frees stage (j + 3) % 4 (read
+  // in step j - 1), start tile j + 3's copies into it, compute.
+  auto step = [&](int j, auto si) __attribute__((always_inline)) {
+    constexpr int S = decltype(si)::value;
+    op_wait_vmcnt<2 * kOpCPW>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    copies(j + 3, stage((S + 3) & 3));
+    compute(j, stage(S));
+  };
+  copies(0, stage(0));
+  copies(1, stage(1));
+  copies(2, stage(2));
+  const int nfull = nt & ~3;
+  int j = 0;
+  for (; j < nfull; j += 4) {
+    step(j, std::integral_constant<int, 0>());
+    step(j + 1, std::integral_constant<int, 1>());
+    step(j + 2, std::integral_constant<int, 2>());
+    step(j + 3, std::integral_constant<int, 3>());
+  }
+  if (j < nt) step(j, std::integral_constant<int, 0>());
+  if (j + 1 < nt) step(j + 1, std::integral_constant<int, 1>());
+  if (j + 2 < nt) step(j + 2, std::integral_constant<int, 2>());
+  op_wait_vmcnt<0>();   // the copies past the end have landed before the workgroup ends
 }
 
 // Split combine fused with the value projection (absorb path, split decode). Workgroup
@@ -433,6 +555,14 @@ bool tuned_out_proj_supported(const gqla_dims* d) {
 hipError_t launch_tuned_out_proj(const ProjParams& p, const float* o_lat, const void* w_uv, void* out, hipStream_t s) {
   const int rows_g = p.rows * (p.H / p.G);
   const int n_rt = (rows_g + 15) / 16;
+  // Many rows: four-wave workgroups sharing each o_lat tile through LDS, about one per CU,
+  // each with at least 8 tiles (the weight load is then small next to the stream).
+  const int nx_stream = std::max(1, kNumCUs / p.G);
+  if (n_rt >= 8 * nx_stream) {
+    out_proj_stream<<<static_cast<unsigned>(nx_stream * p.G), 256, 0, s>>>(p, o_lat, static_cast<const bf16_t*>(w_uv),
+                                                                           static_cast<bf16_t*>(out), nx_stream);
+    return hipGetLastError();
+  }
   // One wave per workgroup (32 rows of W_UV^g, z = which 32), so that the weight and
   // latent-output reads spread over many CUs. Each wave loads its 32 KiB of W_UV^g once;
   // with many row tiles a wave visits at least 4 of them so that weight reloads stay small
