@@ -228,7 +228,6 @@ __global__ __launch_bounds__(64) void out_proj_kernel(ProjParams d, const float*
 // (global_load_lds, three tiles ahead). Every latent output is then read from memory once,
 // instead of once per 32 output features by the single-wave form.
 constexpr int kOpTileBytes = 16 * kDC * 4;             // 16 rows of fp32 o_lat: 32 KiB
-constexpr int kOpStages = 4;
 constexpr int kOpCPW = kOpTileBytes / 1024 / 4;        // 1 KiB copies per wave per tile (8)
 
 template <int N>
@@ -237,9 +236,20 @@ __device__ __forceinline__ void op_wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
 }
 
+__device__ __forceinline__ void op_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __global__ __launch_bounds__(256, 1) void out_proj_stream(ProjParams d, const float* o_lat, const bf16_t* w_uv,
                                                           bf16_t* out, int nx) {
-  __shared__ __attribute__((aligned(16))) char ring[kOpStages * kOpTileBytes];
+  // One array per stage: the compiler then sees that the copies into one stage do not
+  // alias the reads of another, and waits only for the copies it must.
+  __shared__ __attribute__((aligned(16))) char ring0[kOpTileBytes];
+  __shared__ __attribute__((aligned(16))) char ring1[kOpTileBytes];
+  __shared__ __attribute__((aligned(16))) char ring2[kOpTileBytes];
+  __shared__ __attribute__((aligned(16))) char hl[2][16 * kDC * 2];   // bf16 high / low parts of one tile
   const int g = blockIdx.x / nx, x = blockIdx.x % nx;
   const int gs = d.H / d.G;
   const int rows_g = d.rows * gs;
@@ -257,11 +267,10 @@ __global__ __launch_bounds__(256, 1) void out_proj_stream(ProjParams d, const fl
 #pragma unroll
       for (int ks = 0; ks < kDC / 32; ++ks) wa[t][ks] = *reinterpret_cast<const bf16x8*>(wsrc + 16 * t * kDC + 32 * ks);
   }
-  auto stage = [&](int S) __attribute__((always_inline)) { return ring + S * kOpTileBytes; };
-  // Copy j of a wave fills LDS chunks (8 wave + j) * 64 + lane of the tile: row (8 wave + j)
-  // / 2 (the same for the whole wave), position p = 64 ((8 wave + j) % 2) + lane of its 128
-  // 16-byte chunks, which holds source chunk p ^ row (rows 0..15), so the 16 rows of an
-  // operand read sit in 16 different bank groups.
+  auto stage = [&](int S) __attribute__((always_inline)) { return S == 0 ? ring0 : S == 1 ? ring1 : ring2; };
+  // Copy j of a wave fills 16-byte chunks (8 wave + j) * 64 + lane of the tile: row
+  // (8 wave + j) / 2 (the same for the whole wave), position p = 64 ((8 wave + j) % 2) + lane
+  // of its 128 chunks, which holds source chunk p ^ row (rows 0..15).
   auto copies = [&](int j, char* st) __attribute__((always_inline)) {
     const int rt = x + min(j, nt - 1) * nx;   // past the end: the last tile again
 #pragma unroll
@@ -275,14 +284,24 @@ __global__ __launch_bounds__(256, 1) void out_proj_stream(ProjParams d, const fl
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(src) + off, (lds_void*)(st + c * 1024), 16, 0, 2);
     }
   };
-  auto compute = [&](int j, const char* st) __attribute__((always_inline)) {
-    const char* rowp = st + col * (kDC * 4);
-    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  // Wave w splits rows 4w .. 4w + 3 of the tile into bf16 high and low parts, once for all
+  // four waves: lane l takes row 4w + l / 16 and its 8-value chunks c = l % 16 + 16 q. Chunk c
+  // of row r is stored at chunk c ^ r of the row in `hl`, so the 16 rows of an operand read
+  // sit in 16 different bank groups.
+  auto split = [&](const char* st) __attribute__((always_inline)) {
+    const int r = 4 * wave + (lane >> 4);
+    f32x4 xs[4][2];
 #pragma unroll
-    for (int ks = 0; ks < kDC / 32; ++ks) {
-      const int c0 = 8 * ks + 2 * grp;
-      const f32x4 x0 = *reinterpret_cast<const f32x4*>(rowp + 16 * (c0 ^ col));
-      const f32x4 x1 = *reinterpret_cast<const f32x4*>(rowp + 16 * ((c0 + 1) ^ col));
+    for (int q = 0; q < 4; ++q) {
+      const int c = (lane & 15) + 16 * q;
+      xs[q][0] = *reinterpret_cast<const f32x4*>(st + r * (kDC * 4) + 16 * ((2 * c) ^ r));
+      xs[q][1] = *reinterpret_cast<const f32x4*>(st + r * (kDC * 4) + 16 * ((2 * c + 1) ^ r));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = (lane & 15) + 16 * q;
+      const f32x4 x0 = xs[q][0], x1 = xs[q][1];
       bf16x8 hi, lo;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
@@ -291,6 +310,25 @@ __global__ __launch_bounds__(256, 1) void out_proj_stream(ProjParams d, const fl
         hi[k] = h;
         lo[k] = static_cast<__bf16>(v - static_cast<float>(h));
       }
+      *reinterpret_cast<bf16x8*>(hl[0] + r * (kDC * 2) + 16 * (c ^ r)) = hi;
+      *reinterpret_cast<bf16x8*>(hl[1] + r * (kDC * 2) + 16 * (c ^ r)) = lo;
+    }
+  };
+  auto compute = [&](int j) __attribute__((always_inline)) {
+    // All operands are read first: with copies in flight the compiler can only wait for the
+    // LDS counter to drain, so reads issued step by step would each wait a full round trip.
+    bf16x8 hs[kDC / 32], ls[kDC / 32];
+#pragma unroll
+    for (int ks = 0; ks < kDC / 32; ++ks) {
+      const int o = col * (kDC * 2) + 16 * ((4 * ks + grp) ^ col);
+      hs[ks] = *reinterpret_cast<const bf16x8*>(hl[0] + o);
+      ls[ks] = *reinterpret_cast<const bf16x8*>(hl[1] + o);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < kDC / 32; ++ks) {
+      const bf16x8 hi = hs[ks], lo = ls[ks];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[t][ks], hi, acc[t], 0, 0, 0);
@@ -309,32 +347,31 @@ __global__ __launch_bounds__(256, 1) void out_proj_stream(ProjParams d, const fl
       }
     }
   };
-  // Tile j in stage j % 4: wait for its copies (j + 1 and j + 2 may stay in flight; the
-  // weight loads went out first), pass the barrier that also frees stage (j + 3) % 4 (read
-  // in step j - 1), start tile j + 3's copies into it, compute.
+  // Tile j in stage j % 3: wait for its copies (j + 1 may stay in flight; the weight loads
+  // went out first), pass the barrier that also frees stage (j + 2) % 3 (split in step
+  // j - 1) and the split buffer (read in step j - 1), start tile j + 2's copies, split,
+  // pass the second barrier, compute.
   auto step = [&](int j, auto si) __attribute__((always_inline)) {
     constexpr int S = decltype(si)::value;
-    op_wait_vmcnt<2 * kOpCPW>();
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    copies(j + 3, stage((S + 3) & 3));
-    compute(j, stage(S));
+    op_wait_vmcnt<kOpCPW>();
+    op_barrier();
+    copies(j + 2, stage((S + 2) % 3));
+    split(stage(S));
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    op_barrier();
+    compute(j);
   };
   copies(0, stage(0));
   copies(1, stage(1));
-  copies(2, stage(2));
-  const int nfull = nt & ~3;
+  const int nfull = nt - nt % 3;
   int j = 0;
-  for (; j < nfull; j += 4) {
+  for (; j < nfull; j += 3) {
     step(j, std::integral_constant<int, 0>());
     step(j + 1, std::integral_constant<int, 1>());
     step(j + 2, std::integral_constant<int, 2>());
-    step(j + 3, std::integral_constant<int, 3>());
   }
   if (j < nt) step(j, std::integral_constant<int, 0>());
   if (j + 1 < nt) step(j + 1, std::integral_constant<int, 1>());
-  if (j + 2 < nt) step(j + 2, std::integral_constant<int, 2>());
   op_wait_vmcnt<0>();   // the copies past the end have landed before the workgroup ends
 }
 
