@@ -391,11 +391,12 @@ __global__ __launch_bounds__(256, (KsShape<MT, RT>::kPerCU)) void hidden_ks(cons
     off[j] = static_cast<uint32_t>(row) * static_cast<uint32_t>(K) * 2u + 16u * piece;
   }
   // Input operand of tile t, step ks: row m0 + 16 t + col (rows past M re-read row M - 1 and
-  // are never stored), elements 64 wave + 32 ks + 8 grp of the chunk.
+  // are never stored), elements 64 wave + 32 ks + 8 grp of the chunk; offsets from row m0.
+  const bf16_t* xbase = x + static_cast<int64_t>(m0) * K;
   uint32_t xoff[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t)
-    xoff[t] = static_cast<uint32_t>(min(m0 + 16 * t + col, M - 1)) * static_cast<uint32_t>(K) + 64 * wave + 8 * grp;
+    xoff[t] = static_cast<uint32_t>(min(16 * t + col, M - 1 - m0)) * static_cast<uint32_t>(K) + 64 * wave + 8 * grp;
 
   auto stage = [](int S) { return g_ks + S * Sh::kStage; };
   auto copies = [&](int c, char* st) {
@@ -409,7 +410,7 @@ __global__ __launch_bounds__(256, (KsShape<MT, RT>::kPerCU)) void hidden_ks(cons
   };
   bf16x8 xb[4][MT][2];
   auto inputs = [&](int c, bf16x8 (&dst)[MT][2]) {
-    const bf16_t* xc = x + min(c, nch - 1) * kKsChunk;
+    const bf16_t* xc = xbase + min(c, nch - 1) * kKsChunk;
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
