@@ -721,6 +721,7 @@ struct AbsorbSpecCta {
     float mv[NT];          // reference of acc for row `col` of each tile (log2 domain)
     uint32_t coff[CPW];    // per-lane source offsets of this wave's copies within a sub-tile
     int v_base[4];
+    i16x4 plo[VB], phi[VB];   // first batch of transposed reads of the next value step
   };
 
   // Copies of sub-tile k (block k / 2, half k % 2) into slot S. Cache-retaining loads: the
@@ -739,27 +740,34 @@ struct AbsorbSpecCta {
   }
 
   template <int SV>
-  __device__ __forceinline__ void value_step(Value& vt, int k) {
-    // The references and P^T of sub-tile k, then the first half of the transposed latent
-    // reads, in flight while the references are agreed; the second half is issued under
-    // the first products.
-    float mh[2][NT];
+  __device__ __forceinline__ i16x4 vtr(const Value& vt, int ft, int second) {
+    const char* tile = sub_buf<SV>() + vt.v * 256;   // features 128 v .. +128
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(tile + vt.v_base[ft & 3] + 128 * (ft >> 2) + second * 16 * kRowBytes));
+  }
+  // The first batch of the next value step's transposed reads, issued at the end of an
+  // iteration: they land while the wave waits for the barrier.
+  template <int SV>
+  __device__ __forceinline__ void value_prefetch(Value& vt) {
+#pragma unroll
+    for (int ft = 0; ft < VB; ++ft) { vt.plo[ft] = vtr<SV>(vt, ft, 0); vt.phi[ft] = vtr<SV>(vt, ft, 1); }
+  }
+  __device__ __forceinline__ void read_mp(int k, float (&mh)[2][NT], bf16x8 (&pb)[NT]) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int h = 0; h < 2; ++h) mh[h][t] = g_sm[k & 1][t][h][col];
-    bf16x8 pb[NT];
     const char* pbuf = g_sp[k & 1];
 #pragma unroll
     for (int t = 0; t < NT; ++t) pb[t] = *reinterpret_cast<const bf16x8*>(pbuf + (t * 64 + lane) * 16);
-    const char* tile = sub_buf<SV>() + vt.v * 256;   // features 128 v .. +128
-    auto tr = [&](int ft, int second) {
-      return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)(tile + vt.v_base[ft & 3] + 128 * (ft >> 2) + second * 16 * kRowBytes));
-    };
+  }
+
+  template <int SV>
+  __device__ __forceinline__ void value_step(Value& vt, int k, float (&mh)[2][NT], bf16x8 (&pb)[NT]) {
+    auto tr = [&](int ft, int second) { return vtr<SV>(vt, ft, second); };
     i16x4 lo[FQ], hi[FQ];
 #pragma unroll
-    for (int ft = 0; ft < VB; ++ft) { lo[ft] = tr(ft, 0); hi[ft] = tr(ft, 1); }
+    for (int ft = 0; ft < VB; ++ft) { lo[ft] = vt.plo[ft]; hi[ft] = vt.phi[ft]; }
     bool mixed = false;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -809,19 +817,29 @@ struct AbsorbSpecCta {
     const int k_next = min(i + 2, n_sub - 1);
     const int32_t id_next = g_ids[k_next >> 1];
     wait_vmcnt<CPW>();                                   // sub-tile i has landed
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's zeroing is written
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's zeroing and reads are done
     lds_barrier();
     issue_sub<(U + 2) % 4>(vt, sub_src(id_next, k_next));
+    // The references and P^T of sub-tile i - 1; the first half of its transposed latent reads
+    // were issued at the end of the previous iteration, the second half goes out under the
+    // first products.
+    float mh[2][NT];
+    bf16x8 pb[NT];
+    if (i >= 1) read_mp(i - 1, mh, pb);
     if (i < n_sub) {   // rows of sub-tile i past the context: zero, so the value product needs no mask
       const int tok0 = (blk_lo * 2 + i) * kSubTok;
       if (tok0 + kSubTok > L) {
+        // Each value wave zeroes the 16 chunks of its own features (the swizzle moves chunks
+        // only within 8-chunk groups), so its own later reads need no barrier.
         char* tile = sub_buf<U>();
         const int valid = max(0, L - tok0);
-        for (int e = valid * kChunks + (threadIdx.x - 256); e < kSubTok * kChunks; e += 256)
-          *reinterpret_cast<uint4*>(tile + 16 * e) = uint4{0u, 0u, 0u, 0u};
+        for (int q = lane; q < (kSubTok - valid) * 16; q += 64)
+          *reinterpret_cast<uint4*>(tile + (valid + (q >> 4)) * kRowBytes + 16 * (16 * vt.v + (q & 15))) =
+              uint4{0u, 0u, 0u, 0u};
       }
     }
-    if (i >= 1) value_step<(U + 3) % 4>(vt, i - 1);
+    if (i >= 1) value_step<(U + 3) % 4>(vt, i - 1, mh, pb);
+    if (i < n_sub) value_prefetch<U>(vt);
     return true;
   }
 
