@@ -23,7 +23,8 @@
 // weight and row reads of a small batch spread over most CUs instead of a few. At large
 // batches the value projection's fp32 latent outputs are the stream and get a form of their
 // own (out_proj_stream: one four-wave workgroup per CU and group, each o_lat tile read once
-// into an LDS ring and shared by the four waves).
+// into an LDS ring and shared by the four waves), and so does the absorbed query
+// (absorb_query_stream: the weight slice in registers, output tiles stored as whole row slices).
 #include "device_common.h"
 #include "gqla_internal.h"
 #include "tuned.h"
@@ -153,6 +154,123 @@ __global__ __launch_bounds__(NW * 64) void absorb_query_kernel(ProjParams d, con
       }
     }
   }
+}
+
+// Absorbed query over many rows (large batches), where the queries and q_abs are the stream:
+// workgroup (group g, latent slice z of 128 features, run of 64-row tiles). The [DN][128]
+// slice of W_UK^g is staged through LDS once and read transposed into registers (the A
+// operand of every tile), so a tile costs only its query loads, 8 KSA MFMAs per wave and the
+// stores; the next tile's queries load under the current tile's products. Rows past the end
+// re-read and re-store the last row (the same values to the same place), so every store is
+// unconditional and the compiler's memory-counter waits stay exact. Each slice copies a
+// quarter of the RoPE part.
+template <int DN>
+__global__ __launch_bounds__(256, 2) void absorb_query_stream(ProjParams d, const bf16_t* q_nope, const bf16_t* q_rope,
+                                                              const bf16_t* w_uk, bf16_t* q_abs, int nx) {
+  __shared__ __attribute__((aligned(16))) char w[DN * kSliceF * 2];
+  constexpr int KS = DN / 32;
+  constexpr int CT = kSliceF / 16;   // 16-feature output tiles of the slice
+  const int nz = kDC / kSliceF;
+  const int x = blockIdx.x % nx, gz = blockIdx.x / nx;
+  const int g = gz / nz, z = gz % nz;
+  const int f0 = z * kSliceF;
+  const int gs = d.H / d.G;
+  const int rows_g = d.rows * gs;
+  const int n_rt = (rows_g + 63) / 64;
+  if (x >= n_rt) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  {
+    const bf16_t* src = w_uk + static_cast<int64_t>(g) * DN * kDC + f0;
+#pragma unroll
+    for (int i = wave; i < DN / 4; i += 4) {
+      const int r = 4 * i + (lane >> 4);
+      const int c = (lane & 15) ^ swz(r);
+      __builtin_amdgcn_global_load_lds(src + r * kDC + 8 * c, (lds_void*)(w + 1024 * i), 16, 0, 0);
+    }
+  }
+  const int dq = kDC + kDR;
+  auto row_of_r = [&](int rt, int r) __attribute__((always_inline)) {
+    return group_row(min(rt * 64 + wave * 16 + r, rows_g - 1), g, gs, d.H);   // past the end: the last row
+  };
+  auto row_of = [&](int rt) __attribute__((always_inline)) { return row_of_r(rt, col); };
+  auto load_q = [&](int rt, bf16x8 (&dst)[KS]) __attribute__((always_inline)) {
+    const int64_t row = row_of(rt);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) dst[ks] = *reinterpret_cast<const bf16x8*>(q_nope + row * DN + 32 * ks + 8 * grp);
+  };
+  bf16x8 qa[KS], qb[KS];
+  load_q(x, qa);
+  __builtin_amdgcn_s_waitcnt(0);   // the weight slice and the first queries have landed
+  __syncthreads();
+  // A operand of feature tile ct, step ks (W^T, 16 latent features x 32 nope values), read
+  // transposed once: lane `col` of each 16-lane group supplies nope row 32 ks + 8 grp +
+  // 4 half + (col >> 2), features 16 ct + 4 (col & 3).
+  bf16x8 wa[CT][KS];
+  {
+    const int src_n = 8 * grp + (col >> 2);
+    const int src_b = 8 * (col & 3);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int r0 = 32 * ks + src_n, r1 = r0 + 4;
+        const int b = 32 * ct + src_b;
+        const char* p0 = w + r0 * 256 + ((((b >> 4) ^ swz(r0)) << 4) | (b & 15));
+        const char* p1 = w + r1 * 256 + ((((b >> 4) ^ swz(r1)) << 4) | (b & 15));
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
+        wa[ct][ks] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+  }
+  // Every wave has its operands before the staging area is reused for the output tiles.
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __syncthreads();
+  // Tile rt from the queries in `cur`; the queries of tile rt_next load into `nxt` first. Two
+  // named buffers alternate (no register copy between tiles, which would wait for the loads).
+  auto tile = [&](int rt, const bf16x8 (&cur)[KS], bf16x8 (&nxt)[KS], int rt_next) __attribute__((always_inline)) {
+    // RoPE quarter z of the wave's 16 rows: 16 values = 32 bytes per row, two lanes per row
+    // (lanes 32.. repeat lanes 0..31: the same bytes to the same place). Its load goes out
+    // before the next tile's queries, so waiting for it leaves those in flight.
+    const int r16 = (lane & 31) >> 1, half = lane & 1;
+    const int64_t orow = group_row(min(rt * 64 + wave * 16 + r16, rows_g - 1), g, gs, d.H);
+    const uint4 rope = *reinterpret_cast<const uint4*>(q_rope + orow * kDR + 16 * z + 8 * half);
+    load_q(min(rt_next, n_rt - 1), nxt);   // past the last tile: the last tile again
+    __builtin_amdgcn_sched_barrier(0);
+    // The tile's 16 rows x 128 features go through this wave's 4 KiB of the (now free) weight
+    // staging area, so the stores are whole 256-byte row slices (16 bytes per lane) instead of
+    // 8-byte pieces: row r's 16-byte chunk c sits at chunk c ^ (r & 15) of its LDS row.
+    char* stage = w + wave * 4096;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ct][ks], cur[ks], acc, 0, 0, 0);
+      bf16_t packed[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) packed[k] = f32_to_bf16(acc[k]);
+      // Lane (row col, grp) holds features 16 ct + 4 grp .. +4: half of 16-byte chunk 2 ct + grp / 2.
+      const int c = 2 * ct + (grp >> 1);
+      *reinterpret_cast<uint2*>(stage + col * 256 + 16 * (c ^ col) + 8 * (grp & 1)) = *reinterpret_cast<uint2*>(packed);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int r = 4 * k + (lane >> 4), c = lane & 15;
+      const uint4 v = *reinterpret_cast<const uint4*>(stage + r * 256 + 16 * (c ^ r));
+      const int64_t orr = row_of_r(rt, r);
+      *reinterpret_cast<uint4*>(q_abs + orr * dq + f0 + 8 * c) = v;
+    }
+    *reinterpret_cast<uint4*>(q_abs + orow * dq + kDC + 16 * z + 8 * half) = rope;
+  };
+  const int nt = (n_rt - x + nx - 1) / nx;   // tiles x, x + nx, ... of this workgroup
+  int j = 0;
+  for (; j + 2 <= nt; j += 2) {
+    tile(x + j * nx, qa, qb, x + (j + 1) * nx);
+    tile(x + (j + 1) * nx, qb, qa, x + (j + 2) * nx);
+  }
+  if (j < nt) tile(x + j * nx, qa, qb, x + (j + 1) * nx);
+  __builtin_amdgcn_s_waitcnt(0);   // the loads past the end have landed before the workgroup ends
 }
 
 __global__ __launch_bounds__(64) void out_proj_kernel(ProjParams d, const float* o_lat, const bf16_t* w_uv, bf16_t* out,
@@ -565,6 +683,21 @@ hipError_t launch_tuned_absorb_query(const ProjParams& p, const void* q_nope, co
                                      void* q_abs, hipStream_t s) {
   const int rows_g = p.rows * (p.H / p.G);
   const int per_row = (kDC / kSliceF) * p.G;
+  {
+    // Many rows: about two workgroups per CU, each streaming at least 16 tiles of 64 rows.
+    const int n_rt64 = (rows_g + 63) / 64;
+    const int nx = std::max(1, 2 * kNumCUs / per_row);
+    if (n_rt64 >= 16 * nx) {
+      const bf16_t* qn = static_cast<const bf16_t*>(q_nope);
+      const bf16_t* qr = static_cast<const bf16_t*>(q_rope);
+      const bf16_t* wk = static_cast<const bf16_t*>(w_uk);
+      bf16_t* qa = static_cast<bf16_t*>(q_abs);
+      const dim3 grid(static_cast<unsigned>(nx * per_row));
+      if (p.dn == 128) absorb_query_stream<128><<<grid, 256, 0, s>>>(p, qn, qr, wk, qa, nx);
+      else absorb_query_stream<64><<<grid, 256, 0, s>>>(p, qn, qr, wk, qa, nx);
+      return hipGetLastError();
+    }
+  }
   const bool wide = static_cast<int64_t>((rows_g + 63) / 64) * per_row >= kNumCUs;
   const int n_rt = wide ? (rows_g + 63) / 64 : (rows_g + 15) / 16;
   const int nx = (std::max(1, std::min(n_rt, kMaxWGs / per_row)) + 7) / 8 * 8;   // row-tile lanes, x8 for grid_pos
