@@ -10,10 +10,11 @@
 // slice of [W_UK^g ; W_UV^g] in registers for the whole run, so the weights are read
 // once per workgroup, while the latent tiles stream through LDS (global_load_lds,
 // double-buffered, the XOR-swizzled layout of the absorb decode). Key rows come out of
-// K^T = W_UK^g C^T, whose accumulator holds 4 consecutive key features of one token
-// (8-byte stores into a 32-feature key slab); value rows come out of V = C W_UV^g^T,
-// whose accumulator holds 4 consecutive tokens of one feature (8-byte stores into a
-// 32-token value half). The RoPE key is copied into every group's K.
+// K^T = W_UK^g C^T, whose accumulator holds 4 consecutive key features of one token; value
+// rows come out of V = C W_UV^g^T, whose accumulator holds 4 consecutive tokens of one
+// feature. Two such accumulators (two feature tiles of a key, two token tiles of a value)
+// are paired across lane rows with v_permlane16_swap so that each lane stores 16 contiguous
+// bytes. The RoPE key is copied into every group's K.
 #include "device_common.h"
 #include "gqla_internal.h"
 #include "tuned.h"
@@ -106,51 +107,73 @@ struct ExpandCta {
       copy16_to_lds(src + dma_off[k], (lds_void*)(etile<BUF>() + (wave * PER_WAVE + k) * 1024));
   }
 
-  // Key rows (K^T = W C^T) or value rows (V = C W^T) of one 64-token tile; the
-  // orientation is a compile-time choice taken under a wave-uniform branch.
+  // Two 8-byte halves (4 bf16 each, in lanes of rows 2m and 2m + 1 of the wave) become one
+  // 16-byte piece per lane: v_permlane16_swap exchanges `a` of the odd rows with `b` of the
+  // even rows, so even-row lanes end with (a of row 2m, a of row 2m + 1) and odd-row lanes
+  // with (b of row 2m, b of row 2m + 1).
+  __device__ __forceinline__ static uint4 pair16(const f32x4& a, const f32x4& b) {
+    bf16_t pa[4], pb[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) { pa[k] = f32_to_bf16(a[k]); pb[k] = f32_to_bf16(b[k]); }
+    const uint2 ua = *reinterpret_cast<const uint2*>(pa), ub = *reinterpret_cast<const uint2*>(pb);
+    const auto x = __builtin_amdgcn_permlane16_swap(ua.x, ub.x, false, false);
+    const auto y = __builtin_amdgcn_permlane16_swap(ua.y, ub.y, false, false);
+    return uint4{x[0], y[0], x[1], y[1]};
+  }
+
+  // Key rows (K^T = W C^T) or value rows (V = C W^T) of one 64-token tile, two 16-token
+  // tiles at a time; the orientation is a compile-time choice taken under a wave-uniform
+  // branch. Every store is a 16-byte piece: 16 lanes x 64 bytes of contiguous slab rows
+  // (keys) or 64 bytes of a value row per lane group (values).
   template <int BUF, bool KEY>
   __device__ __forceinline__ void tiles(bf16_t* chunk) {
     const char* tile = etile<BUF>();
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-      const char* rows = tile + tt * 16 * kRowBytes;
-      auto ld = [&](int ks) {
+    for (int hp = 0; hp < 2; ++hp) {
+      f32x4 acc[2][2];   // [16-token tile 2 hp + u][ft]
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int ft = 0; ft < 2; ++ft) acc[u][ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+      auto ld = [&](int u, int ks) {
+        const char* rows = tile + (2 * hp + u) * 16 * kRowBytes;
         return *reinterpret_cast<const bf16x8*>(rows + ((ks & 1) ? base_odd : base_even) + 128 * (ks >> 1));
       };
-      bf16x8 a0 = ld(0), a1 = ld(1);
+      bf16x8 a0[2] = {ld(0, 0), ld(1, 0)}, a1[2] = {ld(0, 1), ld(1, 1)};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        bf16x8 a2 = a1;
-        if (ks + 2 < KS) a2 = ld(ks + 2);
+        bf16x8 a2[2] = {a1[0], a1[1]};
+        if (ks + 2 < KS) { a2[0] = ld(0, ks + 2); a2[1] = ld(1, ks + 2); }
 #pragma unroll
-        for (int ft = 0; ft < 2; ++ft) {
-          if (KEY) acc[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[ft][ks], a0, acc[ft], 0, 0, 0);
-          else acc[ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, wf[ft][ks], acc[ft], 0, 0, 0);
-        }
-        a0 = a1;
-        a1 = a2;
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int ft = 0; ft < 2; ++ft) {
+            if (KEY) acc[u][ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[ft][ks], a0[u], acc[u][ft], 0, 0, 0);
+            else acc[u][ft] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[u], wf[ft][ks], acc[u][ft], 0, 0, 0);
+          }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) { a0[u] = a1[u]; a1[u] = a2[u]; }
         __builtin_amdgcn_sched_barrier(0);
       }
+      // Offset of a lane's 16 bytes inside its 32-value run: 16 (grp & 1) + 8 (grp >> 1) values.
+      const int off = 16 * (grp & 1) + 8 * (grp >> 1);
+      if (KEY) {
+        // K^T tile u: lane = token 16 (2 hp + u) + col; ft 0 / 1 hold key features
+        // row0 + 4 grp / row0 + 16 + 4 grp (.. +4) of the 32-feature slab row0 / 32.
 #pragma unroll
-      for (int ft = 0; ft < 2; ++ft) {
-        bf16_t packed[4];
+        for (int u = 0; u < 2; ++u) {
+          const uint4 v = pair16(acc[u][0], acc[u][1]);
+          const int tok = (2 * hp + u) * 16 + col;
+          *reinterpret_cast<uint4*>(chunk + (row0 / kSlab) * kBlock * kSlab + tok * kSlab + off) = v;
+        }
+      } else {
+        // V tile u: lane = value feature row0 + 16 ft + col, tokens 32 hp + 16 u + 4 grp (.. +4)
+        // of the 32-token half hp.
 #pragma unroll
-        for (int k = 0; k < 4; ++k) packed[k] = f32_to_bf16(acc[ft][k]);
-        if (KEY) {
-          // K^T tile: lane = token tt*16 + col, key features f = row0 + 16*ft + 4*grp + k,
-          // inside the 32-feature slab f / 32
-          const int tok = tt * 16 + col;
-          const int f = row0 + 16 * ft + 4 * grp;
-          *reinterpret_cast<uint2*>(chunk + (f / kSlab) * kBlock * kSlab + tok * kSlab + f % kSlab) =
-              *reinterpret_cast<uint2*>(packed);
-        } else {
-          // V tile: lane = value feature f = row0 + 16*ft + col, tokens tok = tt*16 + 4*grp + k,
-          // inside the 32-token half tok / 32
+        for (int ft = 0; ft < 2; ++ft) {
+          const uint4 v = pair16(acc[0][ft], acc[1][ft]);
           const int f = row0 + 16 * ft + col;
-          const int tok = tt * 16 + 4 * grp;
-          *reinterpret_cast<uint2*>(chunk + kBlock * k_feats + (tok / kHalf) * kDV * kHalf + f * kHalf + tok % kHalf) =
-              *reinterpret_cast<uint2*>(packed);
+          *reinterpret_cast<uint4*>(chunk + kBlock * k_feats + hp * kDV * kHalf + f * kHalf + off) = v;
         }
       }
     }
