@@ -72,7 +72,20 @@ def _fill(t, gen, scale=1.0, chunk=1 << 30):
         flat[lo:hi] = (torch.randn(hi - lo, generator=gen, device="cuda") * scale).to(t.dtype)
 
 
-def run_workload(name, reps, gen, flush, rope_shared=1):
+def _graph_time(fn, reps, flush):
+    """Median and best of `fn` captured once in a HIP graph and replayed (the same flush
+    before every replay): the path's time without the host launch gaps between its kernels."""
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    t = _time(g.replay, reps, flush)
+    del g
+    return t
+
+
+def run_workload(name, reps, gen, flush, rope_shared=1, graph=False):
     from workloads import workload
     w = workload(name)
     B = w.batch
@@ -152,7 +165,11 @@ def run_workload(name, reps, gen, flush, rope_shared=1):
         kv = float(ctx.sum()) * dq * elt
         flops = vis(s) * w.heads * 2 * (2 * w.latent + w.rope)
         bound = "mfma" if flops / kv > MFMA_PEAK / HBM_PEAK else "hbm"
-        record("absorb", s, d, t_med, t_best, kv, flops, bound)
+        extra = None
+        if graph:
+            g_med, g_best = _graph_time(absorb, reps, flush)
+            extra = {"graph_ms": g_med * 1e3, "graph_best_ms": g_best * 1e3}
+        record("absorb", s, d, t_med, t_best, kv, flops, bound, extra)
         del q_nope, q_rope, q_abs, o_lat, out, wsa
     del latent
     torch.cuda.empty_cache()
@@ -176,8 +193,11 @@ def run_workload(name, reps, gen, flush, rope_shared=1):
         t_med, t_best = _time(gqa, reps, flush)
         kv = float(ctx.sum()) * per_tok
         flops = vis(s) * w.heads * 2 * (w.qk + w.v)
-        record("gqa", s, d, t_med, t_best, kv, flops, "hbm",
-               {"gqa_expanded_layout": "shared-rope" if shared else "per-group"})
+        extra = {"gqa_expanded_layout": "shared-rope" if shared else "per-group"}
+        if graph:
+            g_med, g_best = _graph_time(gqa, reps, flush)
+            extra.update({"graph_ms": g_med * 1e3, "graph_best_ms": g_best * 1e3})
+        record("gqa", s, d, t_med, t_best, kv, flops, "hbm", extra)
         # append path: the s new tokens of every sequence, latent rows + RoPE + expansion
         # (needs a latent pool too; a small one would not match the block table, so it is
         # timed only where both caches fit next to each other)
@@ -261,6 +281,12 @@ def table(rows):
         out.append(f"| {r['workload']} | {r['path']} | {r['s_q']} | {r['batch']} | {r['ms']:.3f} | {r['best_ms']:.3f} | "
                    f"{r['tokens_per_s']:,.0f} | {r['kv_GBps']:,.0f} | {r['hbm_frac'] * 100:.1f} | {r['tflops']:.0f} | "
                    f"{r['mfma_frac'] * 100:.1f} | {r['bound']} | {r['splits']} |")
+    gr = [r for r in rows if "graph_ms" in r]
+    if gr:
+        out += ["", "| workload | path | s_q | ms (median) | captured in a HIP graph: ms (median) | best ms | eager minus graph |",
+                "|---|---|---|---|---|---|---|"]
+        out += [f"| {r['workload']} | {r['path']} | {r['s_q']} | {r['ms']:.4f} | {r['graph_ms']:.4f} | "
+                f"{r['graph_best_ms']:.4f} | {(r['ms'] - r['graph_ms']) * 1e3:.1f} us |" for r in gr]
     app = [r for r in rows if r["path"] == "append"]
     if app:
         out += ["", "| workload | append: tokens | ms (median) | us per token |", "|---|---|---|---|"]
@@ -281,6 +307,8 @@ def main(argv=None):
     ap.add_argument("--output-side", default="llama3-8b-b32-ctx8k,dsv3-b64-ctx8k",
                     help="workloads whose output side (W_O, folded or not) is timed; empty for none")
     ap.add_argument("--out", default=None)
+    ap.add_argument("--graph", action="store_true",
+                    help="also time each decode path captured in a HIP graph and replayed (graph_ms)")
     a = ap.parse_args(argv)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(2025)
@@ -288,7 +316,7 @@ def main(argv=None):
     rows = []
     for name in filter(None, a.workloads.split(",")):
         print(f"[sweep] {name}", file=sys.stderr, flush=True)
-        rows += run_workload(name, a.reps, gen, flush)
+        rows += run_workload(name, a.reps, gen, flush, graph=a.graph)
     for name in filter(None, a.output_side.split(",")):
         print(f"[sweep] output side {name}", file=sys.stderr, flush=True)
         rows += run_output_side(name, a.reps, gen, flush)
