@@ -490,7 +490,7 @@ def main(argv=None):
         print(json.dumps(t, indent=1))
         return
     if a.gpus != 1:
-        print(f"bench.py measures one GPU: --gpus {a.gpus} is not supported (this build has no "
+        print(f"bench.py measures one GPU: --gpus {a.gpus} is not supported (the library has no "
               "multi-GPU path; the GQA path would shard its groups across ranks)", file=sys.stderr)
         sys.exit(2)
     import torch
