@@ -36,9 +36,11 @@ constexpr int kChunks = kDQ / 8;
 constexpr int kTileBytes = kBlock * kRowBytes;
 constexpr int kDV = 128;
 
-// Chunk swizzle of the latent tile in LDS (the absorb decode's layout: conflict-free
-// 16-row reads of one chunk on gfx950's 256-byte-per-cycle LDS).
-__device__ __forceinline__ int swz(int t) { return (t & 7) ^ ((t >> 3) & 1); }
+// Chunk swizzle of the latent tile in LDS: chunk c of token row t sits at c xor swz(t)
+// inside its 8-chunk group, swz(t) = 2 (t0 xor t3) + 4 t1, the absorb decode's layout. Chosen
+// by measurement: against (t mod 8) xor t3 the expansion is 1.5-4% faster at 8 and 16 groups
+// (same bits out; the operand reads take one chunk of each of 16 rows).
+__device__ __forceinline__ int swz(int t) { return 2 * ((t ^ (t >> 3)) & 1) + 4 * ((t >> 1) & 1); }
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
