@@ -11,7 +11,8 @@
 // registers:
 //   * one workgroup = (sequence, group, split); its waves take interleaved 64-token
 //     blocks of the split and keep private online-softmax states, merged in LDS at
-//     the end;
+//     the end; when sequences x groups do not cover the CUs, a workgroup instead takes
+//     one of the equal runs of the batch's blocks laid end to end (attend_balanced);
 //   * scores are formed transposed, S^T = K Q^T (v_mfma_f32_16x16x32_bf16, A = 16
 //     tokens x 32 features of K, B = 32 features x 16 query rows), so each lane owns
 //     one query row: its running max/sum need only two cross-lane shuffles per step;
@@ -63,7 +64,8 @@ __device__ __forceinline__ float xor_sum(float v) {
 // workgroups of one sequence's groups are placed on one XCD so that area is fetched from
 // HBM once and served to the other groups from that XCD's L2.
 template <int DQK, int DV, int kWaves, int RT, bool SHARED>
-__global__ __launch_bounds__(kWaves * 64, RT == 1 ? 2 : 1) void gqa_decode_split(AttnParams p) {
+__device__ __forceinline__ void attend(const AttnParams& p, int b, int g, int blk_lo, int blk_end, int slot,
+                                       int limit_blocks) {
   constexpr int KS = DQK / 32;     // k-steps of the score product
   constexpr int KSN = SHARED ? (DQK - 64) / 32 : KS;   // k-steps held in the group chunk
   constexpr int KF = 32 * KSN;     // K features in the group chunk
@@ -78,28 +80,12 @@ __global__ __launch_bounds__(kWaves * 64, RT == 1 ? 2 : 1) void gqa_decode_split
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15;          // query row owned by this lane in each tile (MFMA column)
   const int grp = lane >> 4;          // k-group of the MFMA operands
-  int split, g, b;
-  if constexpr (SHARED) {
-    // id = ((u / 8) * G + g) * 8 + u % 8 for unit u = (sequence, split): a unit's groups
-    // share an XCD (ids equal mod 8) and are dispatched together.
-    const int x = blockIdx.x & 7, y = blockIdx.x >> 3;
-    g = y % p.kv_heads;
-    const int u = (y / p.kv_heads) * 8 + x;
-    if (u >= p.B * p.n_split) return;
-    split = u % p.n_split;
-    b = u / p.n_split;
-  } else {
-    split = blockIdx.x % p.n_split;
-    const int bg = blockIdx.x / p.n_split;
-    g = bg % p.kv_heads;
-    b = bg / p.kv_heads;
-  }
   const int gs = p.heads_per_kv;
   const int rows = gs * p.s_q;
 
   const int L = p.ctx_lens[b];
   const int nblk = (L + kBlock - 1) / kBlock;
-  bool bad = (L < p.s_q) || (L > p.max_blocks * kBlock) || (nblk > p.n_split * p.blocks_per_split);
+  bool bad = (L < p.s_q) || (L > p.max_blocks * kBlock) || (nblk > limit_blocks);
 
   // This lane's query rows (one per tile) and their visible-token limits; B operand of S^T:
   // Q^T slices (features 32*ks + 8*grp .. +8 of query row 16*r + col).
@@ -134,8 +120,7 @@ __global__ __launch_bounds__(kWaves * 64, RT == 1 ? 2 : 1) void gqa_decode_split
 
   const bf16_t* kv = static_cast<const bf16_t*>(p.kv);
   const int32_t* table = p.block_table + static_cast<int64_t>(b) * p.max_blocks;
-  const int blk_lo = split * p.blocks_per_split;
-  const int blk_hi = bad ? blk_lo : min(nblk, blk_lo + p.blocks_per_split);
+  const int blk_hi = bad ? blk_lo : min(nblk, blk_end);
   // This wave's blocks: first, first + kWaves, ... (n_my of them).
   const int first = blk_lo + wave;
   const int n_my = blk_hi > first ? (blk_hi - first + kWaves - 1) / kWaves : 0;
@@ -338,17 +323,122 @@ __global__ __launch_bounds__(kWaves * 64, RT == 1 ? 2 : 1) void gqa_decode_split
       *reinterpret_cast<uint4*>(static_cast<bf16_t*>(p.out) + row * DV + f0) = *reinterpret_cast<uint4*>(packed);
       if (p.lse != nullptr && f0 == 0) p.lse[row] = any_bad ? nan_f32() : (M + __log2f(l_tot)) * kLn2;
     } else {
-      const int64_t slot = row * p.n_split + split;
+      const int64_t at = row * p.n_split + slot;
       const bool empty = !(l_tot > 0.f);
-      float* dst = p.ws_o + slot * DV + f0;
+      float* dst = p.ws_o + at * DV + f0;
 #pragma unroll
       for (int k = 0; k < 8; k += 4) {
         f32x4 v;
         for (int u = 0; u < 4; ++u) v[u] = any_bad ? nan_f32() : (empty ? 0.f : o[k + u] / l_tot);
         *reinterpret_cast<f32x4*>(dst + k) = v;
       }
-      if (f0 == 0) p.ws_lse[slot] = any_bad ? nan_f32() : (empty ? -INFINITY : (M + __log2f(l_tot)) * kLn2);
+      if (f0 == 0) p.ws_lse[at] = any_bad ? nan_f32() : (empty ? -INFINITY : (M + __log2f(l_tot)) * kLn2);
     }
+  }
+}
+
+// Blocks of sequence b as the balanced plan counts them: a sequence whose length the
+// kernel rejects (it only writes NaN partials) counts as one block.
+__device__ __forceinline__ int plan_blocks(const AttnParams& p, int b) {
+  if (b >= p.B) return 0;
+  const int L = p.ctx_lens[b];
+  if (L < p.s_q || L > p.max_blocks * kBlock) return 1;
+  const int n = (L + kBlock - 1) / kBlock;
+  return n > p.decl_blocks ? 1 : n;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(v, d, 64);
+    if (lane >= d) v += u;
+  }
+  return v;
+}
+
+// Length-balanced plan: run c of group g covers blocks [c*C, (c+1)*C) of the batch's
+// blocks laid end to end (C = max(ceil(total / chunks), chunk_min)), one piece per sequence
+// it meets; the piece of sequence b goes to partial slot c - floor(start_b / C). The run
+// that holds a sequence's last block also marks that sequence's unused slots empty
+// (lse = -inf, which the combine skips). Every wave derives the plan itself from the
+// context lengths (at most 256 sequences: 4 per lane).
+template <int DQK, int DV, int kWaves, int RT, bool SHARED>
+__device__ __forceinline__ void attend_balanced(const AttnParams& p, int c, int g) {
+  const int lane = threadIdx.x & 63;
+  int ends[4];   // inclusive prefix of plan_blocks over sequences 64 k + lane
+  int carry = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    ends[k] = wave_scan(plan_blocks(p, 64 * k + lane)) + carry;
+    carry = __builtin_amdgcn_readlane(ends[k], 63);
+  }
+  const int total = carry;
+  const int C = max((total + p.chunks - 1) / p.chunks, p.chunk_min);
+  const int lo = c * C;
+  if (lo >= total) return;
+  const int hi = min(total, lo + C);
+  // First sequence whose blocks end past lo, and where its blocks start; the walk from
+  // there on keeps only scalars, so nothing of the scan stays live in the streaming loop.
+  int b = 0;
+#pragma unroll
+  for (int k = 3; k >= 0; --k) {
+    const uint64_t m = __ballot(64 * k + lane < p.B && ends[k] > lo);
+    if (m != 0) b = 64 * k + __builtin_ctzll(m);
+  }
+  const int bk = b >> 6, bl = b & 63;
+  int e = bk == 0 ? __builtin_amdgcn_readlane(ends[0], bl) : bk == 1 ? __builtin_amdgcn_readlane(ends[1], bl)
+        : bk == 2 ? __builtin_amdgcn_readlane(ends[2], bl) : __builtin_amdgcn_readlane(ends[3], bl);
+  e -= plan_blocks(p, b);   // the end of the blocks before sequence b
+  const int gs = p.heads_per_kv;
+  const int rows = gs * p.s_q;
+  for (bool first = true; b < p.B; ++b, first = false) {
+    const int s0 = e;
+    e += plan_blocks(p, b);
+    if (s0 >= hi) break;
+    if (!first) __syncthreads();   // the previous piece's merge has read the LDS
+    const int slot = c - s0 / C;
+    attend<DQK, DV, kWaves, RT, SHARED>(p, b, g, max(lo, s0) - s0, min(hi, e) - s0, slot, p.decl_blocks);
+    if (e <= hi) {
+      const int used = (e - 1) / C - s0 / C + 1;
+      for (int item = threadIdx.x; item < rows * (p.n_split - used); item += kWaves * 64) {
+        const int jr = item % rows, sl = used + item / rows;
+        const int64_t row = static_cast<int64_t>(b * p.s_q + jr / gs) * p.H + g * gs + jr % gs;
+        p.ws_lse[row * p.n_split + sl] = -INFINITY;
+      }
+    }
+  }
+}
+
+// BAL: the length-balanced plan (its own instantiation, so the planning code does not
+// change the register allocation of the streaming loop in the other one).
+template <int DQK, int DV, int kWaves, int RT, bool SHARED, bool BAL>
+__global__ __launch_bounds__(kWaves * 64, RT == 1 ? 2 : 1) void gqa_decode_split(AttnParams p) {
+  const int units = BAL ? p.chunks : p.B * p.n_split;
+  int u, g;
+  if constexpr (SHARED) {
+    // id = ((u / 8) * G + g) * 8 + u % 8 for unit u = (sequence, split) or balanced run: a
+    // unit's groups share an XCD (ids equal mod 8) and are dispatched together.
+    const int x = blockIdx.x & 7, y = blockIdx.x >> 3;
+    g = y % p.kv_heads;
+    u = (y / p.kv_heads) * 8 + x;
+    if (u >= units) return;
+  } else if constexpr (BAL) {
+    u = blockIdx.x % units;
+    g = blockIdx.x / units;
+  } else {
+    const int split = blockIdx.x % p.n_split, bg = blockIdx.x / p.n_split;
+    g = bg % p.kv_heads;
+    u = (bg / p.kv_heads) * p.n_split + split;
+  }
+  if constexpr (BAL) {
+    attend_balanced<DQK, DV, kWaves, RT, SHARED>(p, u, g);
+  } else {
+    const int split = u % p.n_split, b = u / p.n_split;
+    const int blk_lo = split * p.blocks_per_split;
+    attend<DQK, DV, kWaves, RT, SHARED>(p, b, g, blk_lo, blk_lo + p.blocks_per_split, split,
+                                        p.n_split * p.blocks_per_split);
   }
 }
 
@@ -378,10 +468,13 @@ int tuned_gqa_min_blocks_per_split() { return 8; }
 template <int DQK, int RT, bool SHARED>
 hipError_t launch_dqk(const AttnParams& p, hipStream_t s) {
   constexpr int kWaves = 4;
-  const int64_t units = static_cast<int64_t>(p.B) * p.n_split;
+  const int64_t units = p.chunks > 0 ? p.chunks : static_cast<int64_t>(p.B) * p.n_split;
   const int64_t wgs = SHARED ? (units + 7) / 8 * 8 * p.kv_heads : units * p.kv_heads;
   if (wgs > 0x7fffffff) return hipErrorInvalidConfiguration;
-  gqa_decode_split<DQK, 128, kWaves, RT, SHARED><<<static_cast<unsigned>(wgs), kWaves * 64, 0, s>>>(p);
+  if (p.chunks > 0)
+    gqa_decode_split<DQK, 128, kWaves, RT, SHARED, true><<<static_cast<unsigned>(wgs), kWaves * 64, 0, s>>>(p);
+  else
+    gqa_decode_split<DQK, 128, kWaves, RT, SHARED, false><<<static_cast<unsigned>(wgs), kWaves * 64, 0, s>>>(p);
   return hipGetLastError();
 }
 

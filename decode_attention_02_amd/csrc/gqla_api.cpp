@@ -81,10 +81,14 @@ float resolve_scale(const gqla_dims* d) {
 
 int elt_bytes(const gqla_dims* d) { return d->dtype == GQLA_BF16 ? 2 : 4; }
 
+int nblk_declared(const gqla_paged* p) { return p->max_ctx_len / gqla::kBlock + (p->max_ctx_len % gqla::kBlock != 0); }
+
 struct Plan {
   int n_split;
   int blocks_per_split;
   bool tuned;
+  int chunks = 0;      // > 0: length-balanced GQA plan (see below)
+  int chunk_min = 0;
 };
 
 // Split-KV plan. Units of independent work are (sequence, group) on the GQA path and
@@ -93,7 +97,7 @@ struct Plan {
 // split long enough to amortise its prologue and the partial-result traffic.
 Plan plan(const gqla_dims* d, const gqla_paged* p, int32_t path) {
   Plan pl{};
-  const int nblk = (p->max_ctx_len + gqla::kBlock - 1) / gqla::kBlock;
+  const int nblk = nblk_declared(p);
   int n;
   if (path == GQLA_PATH_GQA) {
     pl.tuned = gqla::tuned_gqa_supported(d);
@@ -115,6 +119,19 @@ Plan plan(const gqla_dims* d, const gqla_paged* p, int32_t path) {
     n = std::max(n, (nblk + gqla::tuned_absorb_max_blocks_per_split() - 1) / gqla::tuned_absorb_max_blocks_per_split());
   pl.blocks_per_split = (nblk + n - 1) / n;
   pl.n_split = (nblk + pl.blocks_per_split - 1) / pl.blocks_per_split;
+  // When the context must be split to cover the CUs and the split count is left to the
+  // plan, the tuned GQA kernel cuts the batch's blocks (sequences laid end to end) into
+  // equal runs per group instead: with ragged lengths, equal splits of each sequence give
+  // the workgroups of the longest one the most blocks while those of the shortest idle.
+  // A sequence of n blocks meets at most ceil(n / run) + 1 runs, which bounds the partial
+  // slots per row; the kernel marks the slots a sequence does not use as empty.
+  if (path == GQLA_PATH_GQA && pl.tuned && p->num_splits == 0 && pl.n_split > 1 && d->batch <= gqla::kNumCUs &&
+      static_cast<int64_t>(d->batch) * nblk < (int64_t{1} << 30)) {
+    pl.chunks = static_cast<int>((gqla::tuned_gqa_target_wgs() + d->num_groups - 1) / d->num_groups);
+    pl.chunk_min = gqla::tuned_gqa_min_blocks_per_split();
+    pl.n_split = std::min(pl.chunks + 1, (nblk + pl.chunk_min - 1) / pl.chunk_min + 1);
+    pl.blocks_per_split = nblk;
+  }
   return pl;
 }
 
@@ -148,6 +165,9 @@ gqla_status run_decode(const gqla_dims* d, const gqla_paged* pg, int32_t path, c
   a.scale = resolve_scale(d);
   a.n_split = pl.n_split;
   a.blocks_per_split = pl.blocks_per_split;
+  a.chunks = pl.chunks;
+  a.chunk_min = pl.chunk_min;
+  a.decl_blocks = nblk_declared(pg);
   const int rows = d->batch * d->s_q * d->num_heads;
   if (gqa) {
     const int dqk = d->nope_dim + d->rope_dim;

@@ -41,6 +41,11 @@ struct AttnParams {
   int32_t v_off, v_half, v_ts, v_fs;   // V(t, f) at v_off + v_half*(t/32) + v_ts*(t%32) + v_fs*f
   float scale;
   int32_t n_split, blocks_per_split;
+  // Length-balanced plan (GQA path, chunks > 0): the batch's blocks, laid end to end in
+  // sequence order, are cut into `chunks` equal runs of at least `chunk_min` blocks per
+  // group; a run may end one sequence and start the next. n_split is then the number of
+  // partial slots per row and `decl_blocks` the blocks of the declared longest context.
+  int32_t chunks, chunk_min, decl_blocks;
   float* ws_o;                   // [B*s_q*H][n_split][dvo]   (n_split > 1)
   float* ws_lse;                 // [B*s_q*H][n_split]        (n_split > 1)
   void* out;                     // [B*s_q*H][dvo]            (n_split == 1)

@@ -121,7 +121,9 @@ gqla_status gqla_absorb_query(const gqla_dims* dims, const void* q_nope, const v
 /*
  * gqla_decode_absorb — every head attends over the shared latent "key head" (step 2).
  *   s_t = scale * <q_abs[b][i][h], [c_t | kr_t]>,  o_lat = sum_t softmax(s)_t c_t,
- * over the visible tokens t of row i; split-KV with an online-softmax merge.
+ * over the visible tokens t of row i; split-KV with an online-softmax merge. With
+ * num_splits = 0 and fewer than 256 (sequence, group) pairs, the batch's blocks are cut
+ * into equal runs per group on the device, from ctx_lens (at most 256 sequences).
  * ("GQLA: Attention latente ...", English abstract: the MQA-absorb path keeps MLA's absorbed
  * form, in which all query heads share one latent key/value head; gqla_attn.py docstring:
  * the absorbed path attends with a single MQA-style head per layer.)
@@ -216,7 +218,9 @@ gqla_status gqla_expand_cache(const gqla_dims* dims, const void* latent_cache, c
 /*
  * gqla_decode_gqa — grouped-query decode over the expanded cache.
  *   out[b][i][h] = sum_t softmax(scale * <q[b][i][h], K[g]_t>)_t V[g]_t,  g = h / gs,
- * over the visible tokens t of row i; split-KV with an online-softmax merge.
+ * over the visible tokens t of row i; split-KV with an online-softmax merge. With
+ * num_splits = 0 and fewer than 256 (sequence, group) pairs, the batch's blocks are cut
+ * into equal runs per group on the device, from ctx_lens (at most 256 sequences).
  * (The gs query heads of a group share one key head and one value head: "Grouped Query
  * Attention (GQA)", section "Fonctionnement de la GQA"; GQLA's GQA path runs that over the
  * latent expanded into G key/value heads: gqla_attn.py docstring, and "GQLA: Attention
@@ -288,7 +292,10 @@ gqla_status gqla_out_hidden(const gqla_dims* dims, int32_t hidden, int32_t folde
 gqla_status gqla_fold_out_weight(const gqla_dims* dims, int32_t hidden, const void* w_o, const void* w_uv,
                                  void* w_fold, void* stream);
 
-/* Number of KV splits the decode call for `path` will use (host arithmetic only). */
+/* Number of partial results per query row the decode call for `path` will form (host
+ * arithmetic only): its KV splits, or, for the GQA path's length-balanced plan (chosen when
+ * num_splits is 0, batch x groups < 256 CUs and the context is split), an upper bound on the
+ * equal block runs one sequence can meet, min(ceil(256 / G) + 1, ceil(max blocks / 8) + 1). */
 gqla_status gqla_num_splits(const gqla_dims* dims, const gqla_paged* paged, int32_t path,
                             int32_t* n);
 

@@ -124,8 +124,13 @@ def test_split_plan_covers_context(path, B, H, Gr, s_q, ctx):
         assert 1 <= n <= min(nblk, 1024)
         if forced:
             assert n <= forced
-        bps = -(-nblk // n)
-        assert (n - 1) * bps < nblk <= n * bps   # no empty trailing split
+        if path == G.GQLA_PATH_GQA and not forced and B * Gr < 256 and nblk >= 16:
+            # length-balanced plan: n counts partial slots per row, bounded by the runs a
+            # sequence can meet (runs of at least 8 blocks, ceil(256 / G) of them per group)
+            assert 2 <= n <= min(-(-256 // Gr) + 1, -(-nblk // 8) + 1)
+        else:
+            bps = -(-nblk // n)
+            assert (n - 1) * bps < nblk <= n * bps   # no empty trailing split
         ws = G.gqla_workspace_bytes(d, path, nblk, ctx, B * nblk, num_splits=forced)
         dvo = 128 if path == 1 else 512
         assert ws == (0 if n == 1 else B * s_q * H * n * (dvo + 1) * 4)
