@@ -24,6 +24,7 @@
 // rows beyond gs * s_q (up to the 16 of an MFMA tile) carry zero queries.
 #include "device_common.h"
 #include "gqla_internal.h"
+#include "balanced_plan.h"
 #include "tuned.h"
 
 #include <cmath>
@@ -337,69 +338,22 @@ __device__ __forceinline__ void attend(const AttnParams& p, int b, int g, int bl
   }
 }
 
-// Blocks of sequence b as the balanced plan counts them: a sequence whose length the
-// kernel rejects (it only writes NaN partials) counts as one block.
-__device__ __forceinline__ int plan_blocks(const AttnParams& p, int b) {
-  if (b >= p.B) return 0;
-  const int L = p.ctx_lens[b];
-  if (L < p.s_q || L > p.max_blocks * kBlock) return 1;
-  const int n = (L + kBlock - 1) / kBlock;
-  return n > p.decl_blocks ? 1 : n;
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_scan(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int u = __shfl_up(v, d, 64);
-    if (lane >= d) v += u;
-  }
-  return v;
-}
-
-// Length-balanced plan: run c of group g covers blocks [c*C, (c+1)*C) of the batch's
-// blocks laid end to end (C = max(ceil(total / chunks), chunk_min)), one piece per sequence
-// it meets; the piece of sequence b goes to partial slot c - floor(start_b / C). The run
-// that holds a sequence's last block also marks that sequence's unused slots empty
-// (lse = -inf, which the combine skips). Every wave derives the plan itself from the
-// context lengths (at most 256 sequences: 4 per lane).
+// Length-balanced plan (balanced_plan.h): run c of group g attends to each piece of the
+// sequences it meets in turn, then marks a finished sequence's unused slots empty.
 template <int DQK, int DV, int kWaves, int RT, bool SHARED>
 __device__ __forceinline__ void attend_balanced(const AttnParams& p, int c, int g) {
-  const int lane = threadIdx.x & 63;
-  int ends[4];   // inclusive prefix of plan_blocks over sequences 64 k + lane
-  int carry = 0;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    ends[k] = wave_scan(plan_blocks(p, 64 * k + lane)) + carry;
-    carry = __builtin_amdgcn_readlane(ends[k], 63);
-  }
-  const int total = carry;
-  const int C = max((total + p.chunks - 1) / p.chunks, p.chunk_min);
-  const int lo = c * C;
-  if (lo >= total) return;
-  const int hi = min(total, lo + C);
-  // First sequence whose blocks end past lo, and where its blocks start; the walk from
-  // there on keeps only scalars, so nothing of the scan stays live in the streaming loop.
-  int b = 0;
-#pragma unroll
-  for (int k = 3; k >= 0; --k) {
-    const uint64_t m = __ballot(64 * k + lane < p.B && ends[k] > lo);
-    if (m != 0) b = 64 * k + __builtin_ctzll(m);
-  }
-  const int bk = b >> 6, bl = b & 63;
-  int e = bk == 0 ? __builtin_amdgcn_readlane(ends[0], bl) : bk == 1 ? __builtin_amdgcn_readlane(ends[1], bl)
-        : bk == 2 ? __builtin_amdgcn_readlane(ends[2], bl) : __builtin_amdgcn_readlane(ends[3], bl);
-  e -= plan_blocks(p, b);   // the end of the blocks before sequence b
+  const BalancedRun run = balanced_run(p, c);
+  if (run.empty) return;
+  const int C = run.C, lo = run.lo, hi = run.hi;
   const int gs = p.heads_per_kv;
   const int rows = gs * p.s_q;
-  for (bool first = true; b < p.B; ++b, first = false) {
+  int e = run.start;
+  for (int b = run.b; b < p.B; ++b) {
     const int s0 = e;
     e += plan_blocks(p, b);
     if (s0 >= hi) break;
-    if (!first) __syncthreads();   // the previous piece's merge has read the LDS
-    const int slot = c - s0 / C;
-    attend<DQK, DV, kWaves, RT, SHARED>(p, b, g, max(lo, s0) - s0, min(hi, e) - s0, slot, p.decl_blocks);
+    if (b != run.b) __syncthreads();   // the previous piece's merge has read the LDS
+    attend<DQK, DV, kWaves, RT, SHARED>(p, b, g, max(lo, s0) - s0, min(hi, e) - s0, c - s0 / C, p.decl_blocks);
     if (e <= hi) {
       const int used = (e - 1) / C - s0 / C + 1;
       for (int item = threadIdx.x; item < rows * (p.n_split - used); item += kWaves * 64) {
