@@ -72,3 +72,28 @@ def test_balanced_plan_out_of_pool_id_poisons_only_its_sequence():
         e = rel_err(out[b], ref[b]["out"])
         log(f"  seq {b}: out {e:.2e}")
         assert e <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("rope_shared", [False, True])
+def test_balanced_plan_many_short_sequences(rope_shared):
+    """200 sequences of one group (16 heads, s_q = 2: 32 rows, two row tiles): the plan's
+    prefix sum runs over all four of each lane's sequences, and most 8-block runs walk several
+    one- to four-block sequences in turn; two long sequences make the context split."""
+    w = workload("dsv3-tp8share-ctx16k", groups=1)
+    rng = np.random.default_rng(7)
+    ctx = [int(c) for c in rng.integers(2, 220, size=200)]
+    ctx[7], ctx[150] = 3000, 2500
+    x = generate(w, 2, batch=len(ctx), ctx_lens=ctx, shuffled=True, extra_blocks=3)
+    run = Run(x, 0, rope_shared)
+    G = run.G
+    n = G.gqla_num_splits(run.dims, G.GQLA_PATH_GQA, run.table.shape[1], run.paged.max_ctx_len, x.num_blocks)
+    log(f"balanced gqa: 200 sequences, one group, rope_shared={rope_shared}, slots={n}")
+    out, lse = _decode(run)
+    ref = oracle_paths(x)
+    worst = 0.0
+    for b in ref:
+        e = rel_err(out[b], ref[b]["out"])
+        le = float(np.max(np.abs(lse[b] - ref[b]["lse"])))
+        worst = max(worst, e)
+        assert e <= TOL["bf16"] and le <= TOL["bf16"] * max(1.0, float(np.max(np.abs(ref[b]["lse"])))), (b, e, le)
+    log(f"  worst out {worst:.2e} over {len(ref)} sequences")
