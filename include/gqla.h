@@ -121,9 +121,7 @@ gqla_status gqla_absorb_query(const gqla_dims* dims, const void* q_nope, const v
 /*
  * gqla_decode_absorb — every head attends over the shared latent "key head" (step 2).
  *   s_t = scale * <q_abs[b][i][h], [c_t | kr_t]>,  o_lat = sum_t softmax(s)_t c_t,
- * over the visible tokens t of row i; split-KV with an online-softmax merge. With
- * num_splits = 0 and fewer than 256 (sequence, group) pairs, the batch's blocks are cut
- * into equal runs per group on the device, from ctx_lens (at most 256 sequences).
+ * over the visible tokens t of row i; split-KV with an online-softmax merge.
  * ("GQLA: Attention latente ...", English abstract: the MQA-absorb path keeps MLA's absorbed
  * form, in which all query heads share one latent key/value head; gqla_attn.py docstring:
  * the absorbed path attends with a single MQA-style head per layer.)
@@ -219,8 +217,9 @@ gqla_status gqla_expand_cache(const gqla_dims* dims, const void* latent_cache, c
  * gqla_decode_gqa — grouped-query decode over the expanded cache.
  *   out[b][i][h] = sum_t softmax(scale * <q[b][i][h], K[g]_t>)_t V[g]_t,  g = h / gs,
  * over the visible tokens t of row i; split-KV with an online-softmax merge. With
- * num_splits = 0 and fewer than 256 (sequence, group) pairs, the batch's blocks are cut
- * into equal runs per group on the device, from ctx_lens (at most 256 sequences).
+ * num_splits = 0, when the (sequence, group) pairs cannot cover the 256 CUs and the context
+ * has to be split (batch <= 256), the batch's blocks are cut into equal runs per group on
+ * the device, from ctx_lens (the length-balanced plan of gqla_num_splits).
  * (The gs query heads of a group share one key head and one value head: "Grouped Query
  * Attention (GQA)", section "Fonctionnement de la GQA"; GQLA's GQA path runs that over the
  * latent expanded into G key/value heads: gqla_attn.py docstring, and "GQLA: Attention
