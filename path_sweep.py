@@ -85,7 +85,7 @@ def _graph_time(fn, reps, flush):
     return t
 
 
-def run_workload(name, reps, gen, flush, rope_shared=1, graph=False):
+def run_workload(name, reps, gen, flush, rope_shared=1, graph=False, block_table="workload"):
     from workloads import workload
     w = workload(name)
     B = w.batch
@@ -95,7 +95,7 @@ def run_workload(name, reps, gen, flush, rope_shared=1, graph=False):
     nbs = (int(lens_h.max()) + 63) // 64
     nblk = (lens_h + 63) // 64
     NB = int(nblk.sum())
-    if w.shuffled:
+    if (w.shuffled and block_table == "workload") or block_table == "shuffled":
         phys = rng.permutation(NB).astype(np.int32)
     else:
         phys = np.arange(NB, dtype=np.int32)
@@ -309,6 +309,9 @@ def main(argv=None):
     ap.add_argument("--out", default=None)
     ap.add_argument("--graph", action="store_true",
                     help="also time each decode path captured in a HIP graph and replayed (graph_ms)")
+    ap.add_argument("--block-table", choices=("workload", "identity", "shuffled"), default="workload",
+                    help="the workload's block table, or every sequence's blocks adjacent (identity), or a "
+                         "seeded permutation of the pool (shuffled)")
     a = ap.parse_args(argv)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(2025)
@@ -316,7 +319,7 @@ def main(argv=None):
     rows = []
     for name in filter(None, a.workloads.split(",")):
         print(f"[sweep] {name}", file=sys.stderr, flush=True)
-        rows += run_workload(name, a.reps, gen, flush, graph=a.graph)
+        rows += run_workload(name, a.reps, gen, flush, graph=a.graph, block_table=a.block_table)
     for name in filter(None, a.output_side.split(",")):
         print(f"[sweep] output side {name}", file=sys.stderr, flush=True)
         rows += run_output_side(name, a.reps, gen, flush)
