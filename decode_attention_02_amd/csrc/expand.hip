@@ -54,6 +54,14 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// The expanded cache is written once here and read by later decode calls, not by this
+// kernel: non-temporal 16-byte stores (6.6-8% faster at 16 groups, 0-6% at 8, no change at
+// 2, than ordinary stores; the same bytes).
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_stream(bf16_t* dst, const uint4& v) {
+  __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(dst));
+}
+
 // One 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4): lane l's bytes
 // land at lds + 16 * l.
 __device__ __forceinline__ void copy16_to_lds(const char* g, lds_void* lds) {
@@ -166,7 +174,7 @@ struct ExpandCta {
         for (int u = 0; u < 2; ++u) {
           const uint4 v = pair16(acc[u][0], acc[u][1]);
           const int tok = (2 * hp + u) * 16 + col;
-          *reinterpret_cast<uint4*>(chunk + (row0 / kSlab) * kBlock * kSlab + tok * kSlab + off) = v;
+          store_stream(chunk + (row0 / kSlab) * kBlock * kSlab + tok * kSlab + off, v);
         }
       } else {
         // V tile u: lane = value feature row0 + 16 ft + col, tokens 32 hp + 16 u + 4 grp (.. +4)
@@ -175,7 +183,7 @@ struct ExpandCta {
         for (int ft = 0; ft < 2; ++ft) {
           const uint4 v = pair16(acc[0][ft], acc[1][ft]);
           const int f = row0 + 16 * ft + col;
-          *reinterpret_cast<uint4*>(chunk + kBlock * k_feats + hp * kDV * kHalf + f * kHalf + off) = v;
+          store_stream(chunk + kBlock * k_feats + hp * kDV * kHalf + f * kHalf + off, v);
         }
       }
     }
@@ -197,7 +205,7 @@ struct ExpandCta {
       const int tok = i / (kDR / 8), c = kDC / 8 + i % (kDR / 8);
       const uint4 v = *reinterpret_cast<const uint4*>(tile + tok * kRowBytes + (((c & ~7) | ((c & 7) ^ swz(tok))) << 4));
       const int fk = kf0 + 8 * (i % (kDR / 8));
-      *reinterpret_cast<uint4*>(kdst + (fk / kSlab) * kBlock * kSlab + tok * kSlab + fk % kSlab) = v;
+      store_stream(kdst + (fk / kSlab) * kBlock * kSlab + tok * kSlab + fk % kSlab, v);
     }
   }
 
