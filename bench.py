@@ -375,8 +375,11 @@ def device_info(torch):
 
 
 def stream_ceilings(torch, gib=4, reps=5):
-    """Practical HBM rates of plain torch kernels on this GPU (context for the roofline: the
-    published 8 TB/s is not reachable by ordinary loads): a read-only reduction and a copy."""
+    """Practical HBM read rates on this GPU, context for the roofline (the published 8 TB/s
+    is not reachable by ordinary loads): gqla_stream_read, the library's plain streaming read
+    with the decodes' load form, best over a few workgroup counts (the decode's ceiling), and
+    two plain torch kernels, a read-only reduction and a copy."""
+    import decode_attention_02_amd as G
     n = gib * (1 << 30) // 4
     src = torch.ones(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
@@ -393,9 +396,17 @@ def stream_ceilings(torch, gib=4, reps=5):
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1) / 1e3)
         return nbytes / float(np.median(ts)) / 1e9
-    out = {"read_sum_GBps": rate(lambda: src.sum(), 4.0 * n), "copy_GBps": rate(lambda: dst.copy_(src), 8.0 * n),
+    partial = torch.empty(65536, dtype=torch.float32, device="cuda")
+    by_wgs = {w: rate(lambda: G.gqla_stream_read(src, partial, w), 4.0 * n) for w in (512, 1024, 2048, 4096, 8192)}
+    got = float(partial[:8192].double().sum())
+    if got != float(n):   # every fp32 one of the buffer is counted exactly once
+        raise RuntimeError(f"gqla_stream_read summed {got} ones, expected {n}")
+    best = max(by_wgs, key=by_wgs.get)
+    out = {"stream_read_GBps": by_wgs[best], "stream_read_wgs": best,
+           "stream_read_by_wgs": {str(k): round(v, 1) for k, v in by_wgs.items()},
+           "read_sum_GBps": rate(lambda: src.sum(), 4.0 * n), "copy_GBps": rate(lambda: dst.copy_(src), 8.0 * n),
            "buffer_GiB": gib}
-    del src, dst
+    del src, dst, partial
     torch.cuda.empty_cache()
     return out
 
@@ -582,6 +593,8 @@ def main(argv=None):
                            "avg_launch_ms": t["decode_ms"], "median_launch_ms": t["decode_median_ms"],
                            "best_launch_ms": t["decode_best_ms"], "launches_timed": a.steps,
                            "splits": res_paths["gqa"]["splits"]}
+        if ceil:   # the same rate against what a plain streaming read of this GPU reaches
+            res["roofline"]["frac_of_stream_read"] = achieved / ceil["stream_read_GBps"]
     if not a.no_cpu_baseline:
         log(f"[bench] timing the fp64 oracle for ~{a.cpu_seconds:.0f} s on {len(bn.sample)} sampled sequences")
         res["cpu_baseline"] = cpu_baseline(bn, a.cpu_seconds)

@@ -23,7 +23,7 @@ EXPORTED = ("gqla_absorb_query", "gqla_decode_absorb", "gqla_out_proj", "gqla_ex
             "gqla_cache_bytes_per_token", "gqla_validate_paged", "gqla_status_string",
             "gqla_last_error", "gqla_version", "gqla_pick_path", "gqla_append_tokens",
             "gqla_out_hidden", "gqla_fold_out_weight", "gqla_decode_absorb_noalloc",
-            "gqla_decode_absorb_out")
+            "gqla_decode_absorb_out", "gqla_stream_read")
 NOALLOC_SCRATCH_BYTES = 64 << 20   # GQLA_NOALLOC_SCRATCH_BYTES
 
 
@@ -70,6 +70,7 @@ def _load() -> ctypes.CDLL:
         "gqla_append_tokens": [D, P, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp],
         "gqla_out_hidden": [D, i32, i32, vp, vp, vp, vp],
         "gqla_fold_out_weight": [D, i32, vp, vp, vp, vp],
+        "gqla_stream_read": [vp, sz, vp, i32, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -263,6 +264,16 @@ def gqla_pick_path(dims: Dims, total_ctx: int, max_ctx: int):
 def gqla_validate_paged(dims: Dims, paged: Paged, stream=None) -> None:
     d, p = dims.c(), paged.c()
     _check(LIB.gqla_validate_paged(ctypes.byref(d), ctypes.byref(p), _stream(stream)), "gqla_validate_paged")
+
+
+def gqla_stream_read(src, partial, num_wgs: int, stream=None) -> None:
+    """Read every byte of the device tensor `src` with the decodes' streaming loads;
+    partial (fp32, at least num_wgs elements) receives one sum per workgroup."""
+    if partial.dtype != torch.float32 or partial.numel() < num_wgs:
+        raise ValueError("partial must be fp32 with at least num_wgs elements")
+    _check(LIB.gqla_stream_read(ctypes.c_void_p(src.data_ptr()), ctypes.c_size_t(src.numel() * src.element_size()),
+                                ctypes.c_void_p(partial.data_ptr()), ctypes.c_int32(num_wgs), _stream(stream)),
+           "gqla_stream_read")
 
 
 def gqla_version() -> str:

@@ -337,6 +337,18 @@ int64_t gqla_cache_bytes_per_token(const gqla_dims* dims, int32_t path);
  * the first offending (b, block) in gqla_last_error(). */
 gqla_status gqla_validate_paged(const gqla_dims* dims, const gqla_paged* paged, void* stream);
 
+/*
+ * gqla_stream_read — measurement helper, not a decode step: reads `bytes` bytes at `src`
+ * (device memory, 16-byte aligned, bytes a non-zero multiple of 16) with the load form the
+ * decodes stream their caches with (non-temporal 128-bit loads covering whole lines), over
+ * num_wgs workgroups of 256 lanes in [1, 65536], and writes each workgroup's fp32 sum of the
+ * data read as fp32 words to partial[num_wgs] (device, caller-owned), so the loads cannot be
+ * dropped. Timing it gives the streaming-read rate the decodes' HBM fraction is set beside.
+ * Errors: GQLA_ERR_INVALID_ARG for NULL pointers, a misaligned src or size, or num_wgs out of
+ * range; GQLA_ERR_HIP if the launch fails.
+ */
+gqla_status gqla_stream_read(const void* src, size_t bytes, float* partial, int32_t num_wgs, void* stream);
+
 const char* gqla_status_string(gqla_status status);
 const char* gqla_last_error(void);
 
