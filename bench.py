@@ -71,6 +71,8 @@ def parse(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--cpu-sample", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-table", action="store_true",
+                    help="time the fp64 oracle in full on the host-sized workloads (no GPU use) and exit")
     ap.add_argument("--flush-mib", type=int, default=1024)
     ap.add_argument("--profile", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -473,6 +475,66 @@ def cpu_baseline(bn, budget_s):
             "single_thread_gqa_tokens_per_s": bn.s_q / (t1 - t0), "host_cpus": os.cpu_count()}
 
 
+def cpu_table(names=None, single_thread_upto=1):
+    """The fp64 oracle, as it stands, timed in full on the four workloads that fit a host run
+    (the tiny layer, LLaMA-3-8B batch 32, DeepSeek-V3 batch 64, the long-context batch 8):
+    every sequence of the batch on each path and s_q the workload runs, with all BLAS threads
+    and, for the first single_thread_upto + 1 workloads, on one thread too. Inputs are the
+    seeded host inputs of each workload (workloads.generate); no GPU is used."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from oracle import gqla_ref as R
+    from workloads import bf16_bits_to_f64, generate, workload
+
+    def f64(a):
+        return bf16_bits_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)
+
+    runs = {"tiny-fp32": [("absorb", 1), ("gqa", 1), ("naive", 1), ("absorb", 2), ("gqa", 2), ("naive", 2)],
+            "llama3-8b-b32-ctx8k": [("absorb", 1), ("gqa", 2)],
+            "dsv3-b64-ctx8k": [("absorb", 1), ("gqa", 1), ("absorb", 2), ("gqa", 2)],
+            "dsv3-b8-ctx32k-64k": [("absorb", 2), ("gqa", 2)]}
+    if names is not None:
+        runs = {n: runs[n] for n in names}
+    threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    rows = []
+    for wi, (name, cases) in enumerate(runs.items()):
+        w = workload(name)
+        sc = R.qk_scale(w.nope, w.rope)
+        for s_q in sorted({c[1] for c in cases}):
+            x = generate(w, s_q)
+            wk, wv = f64(x.w_uk), f64(x.w_uv)
+            seqs = [(f64(x.c_kv_seq[b]), f64(x.k_rope_seq[b]), f64(x.q_nope[b]), f64(x.q_rope[b]))
+                    for b in range(len(x.ctx_lens))]
+
+            def one(path, c, kr, qn, qr):
+                if path == "gqa":
+                    K, V = R.expand_latent(c, kr, wk, wv)
+                    R.gqa_attention(np.concatenate([qn, qr], axis=-1), K, V, s_q, sc)
+                elif path == "absorb":
+                    o_lat, _ = R.absorb_attention(R.absorb_query(qn, qr, wk), c, kr, s_q, sc)
+                    R.out_projection(o_lat, wv)
+                else:
+                    R.mla_expanded_attention(c, kr, wk, wv, qn, qr, s_q, sc)
+
+            for path, sq in cases:
+                if sq != s_q:
+                    continue
+                for nthr in ([threads, 1] if wi <= single_thread_upto else [threads]):
+                    with threadpool_limits(limits=nthr):
+                        t0 = time.perf_counter()
+                        for sqn in seqs:
+                            one(path, *sqn)
+                        t = time.perf_counter() - t0
+                    r = {"workload": name, "path": path, "s_q": s_q, "batch": len(seqs),
+                         "context": [int(x.ctx_lens.min()), int(x.ctx_lens.max())], "threads": nthr,
+                         "seconds": t, "tokens_per_s": len(seqs) * s_q / t}
+                    rows.append(r)
+                    log(f"[cpu-table] {name} {path} s_q={s_q} threads={nthr}: {t:.2f} s, {r['tokens_per_s']:.1f} tokens/s")
+            del x, seqs
+    return {"kind": "oracle", "unit": "tokens/s", "cores": int(threads), "host_cpus": os.cpu_count(),
+            "note": "fp64 NumPy oracle over every sequence of each batch (not sampled), seeded host inputs",
+            "rows": rows}
+
+
 def path_record(bn, name, r, kv, flops, s_q, splits):
     ms = r["ms"]
     d = {"s_q": s_q, "ms": ms, "median_ms": r["median_ms"], "best_ms": r["best_ms"], "wall_ms": r["wall_ms"],
@@ -499,6 +561,9 @@ def main(argv=None):
         if a.store_traffic:
             store_traffic(t)
         print(json.dumps(t, indent=1))
+        return
+    if a.cpu_table:
+        print(json.dumps({"cpu_table": cpu_table()}), flush=True)
         return
     if a.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {a.gpus} is not supported (the library has no "

@@ -63,3 +63,15 @@ def test_stored_traffic_is_used_only_for_the_same_source_workload_and_layout(tmp
     assert bench.load_traffic("w", "per-group") is None
     f.write_text(json.dumps(dict(good, source_sha256="0" * 64)))        # kernel changed since
     assert bench.load_traffic("w", "shared-rope") is None
+
+
+def test_cpu_table_times_every_case_of_the_tiny_layer():
+    """bench.py --cpu-table's oracle timing on the tiny layer: every path and s_q the layer
+    runs, on all BLAS threads and on one."""
+    import bench
+    t = bench.cpu_table(names=["tiny-fp32"])
+    assert t["kind"] == "oracle" and t["cores"] >= 1
+    got = {(r["path"], r["s_q"], r["threads"]) for r in t["rows"]}
+    want = {(p, s, n) for p in ("absorb", "gqa", "naive") for s in (1, 2) for n in {t["cores"], 1}}
+    assert got == want
+    assert all(r["batch"] == 2 and r["seconds"] > 0 and r["tokens_per_s"] > 0 for r in t["rows"])
